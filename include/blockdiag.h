@@ -1,0 +1,213 @@
+/*
+ * blockdiag.h -- C ABI of the block-diagonal (per-document causal) packed
+ * attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (Automodel page "feat(distributed): block-diagonal varlen
+ * CP for packed sequences"):
+ *   - Summary / Motivation: a packed row holds several documents back to back;
+ *     a query attends a key only inside its own document and only at or before
+ *     its own position (block-causal), exactly as a dense masked SDPA would.
+ *   - Design overview, batch.py and packed.py; key property 1: one GPU holds a
+ *     contiguous chunk of query rows [row_offset, row_offset + q_len) of every
+ *     batch row and the K/V of the whole row; row_offset = 0 with q_len = S is
+ *     the single-GPU packed case.
+ *   - Summary and Design overview, kernels.py: the varlen kernel is driven by
+ *     cu_seqlens metadata that is computed and validated on the host once per
+ *     step, so no layer needs a host sync and no bad offset reaches a kernel.
+ *   - key property 2: a document that starts left of the chunk gives its first
+ *     segment more keys than queries, aligned bottom-right.
+ *
+ * Conventions shared by every call:
+ *   - Every function returns a bd_status; nothing throws across the ABI.  On a
+ *     non-OK status blockdiag_last_error() returns a message (thread-local,
+ *     valid until the next call on the same thread).
+ *   - Argument checks run on the host before anything is enqueued: a call that
+ *     returns an error has launched nothing.
+ *   - "device" pointers are HIP device memory; "host" pointers are ordinary
+ *     host memory.  The caller allocates and owns every buffer; the library
+ *     never allocates or frees memory, keeps no pointer after returning, and
+ *     creates no stream.  Work is enqueued on the caller's stream (a
+ *     hipStream_t passed as void*; NULL = the default stream) with no host
+ *     synchronisation.  A fault during execution surfaces at the caller's next
+ *     synchronisation.
+ *   - Tensors are dense, row-major, contiguous:
+ *       q, o, dO, dq : [batch][q_len][h_q][head_dim]
+ *       k, v, dk, dv : [batch][seq_len][h_kv][head_dim]   (whole packed row)
+ *       lse          : [batch][h_q][q_len] float32, natural log of the softmax
+ *                      denominator in units of scaled logits; -inf on rows
+ *                      that attend no key (padding)
+ *     Element type: float32 (BD_F32) or bfloat16 (BD_BF16) for every tensor
+ *     except lse (always float32).  Grouped-query attention: query head h reads
+ *     K/V head h / (h_q / h_kv).
+ *   - Padding: positions past the sum of a row's document lengths belong to no
+ *     document.  A padding query row gets O = 0, LSE = -inf, dQ = 0; a key no
+ *     local row attends gets dK = dV = 0.
+ */
+#ifndef BLOCKDIAG_H
+#define BLOCKDIAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BD_OK = 0,
+  BD_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size    */
+  BD_ERR_BAD_METADATA = 2,  /* document lengths or segment table malformed    */
+  BD_ERR_CAPACITY = 3,      /* output arrays too small; *n_seg holds the need */
+  BD_ERR_WORKSPACE = 4,     /* workspace smaller than blockdiag_workspace_bytes */
+  BD_ERR_UNSUPPORTED = 5,   /* valid but not implemented (dtype, head_dim)    */
+  BD_ERR_HIP = 6            /* the HIP runtime refused a launch               */
+} bd_status;
+
+typedef enum { BD_F32 = 0, BD_BF16 = 1 } bd_dtype;
+
+/*
+ * blockdiag_segment -- varlen segment table of one chunk (host only, integer
+ * only, deterministic).  Summary: per-step precomputed cu_seqlens; Design
+ * overview, kernels.py: varlen segmentation plus host-side validation.  Call
+ * once per step; every layer reuses the result.
+ *
+ * Inputs (host):
+ *   doc_lens[sum(docs_per_row)]  document lengths of all batch rows, row after
+ *                                row; each >= 0 (a zero-length document holds
+ *                                no token); per row the sum is <= seq_len and
+ *                                the rest of the row is padding.
+ *   docs_per_row[batch]          number of documents in each row (>= 0).
+ *   batch >= 0, seq_len >= 0, 0 <= row_offset, 0 <= q_len,
+ *   row_offset + q_len <= seq_len.
+ *   capacity                     entries available in the output arrays
+ *                                (cu arrays must hold capacity + 1).
+ * Outputs (host), one segment per (row, document meeting the chunk), in row
+ * then position order, plus one padding segment per row whose padding tail
+ * reaches into the chunk:
+ *   cu_seqlens_q[n+1]  local query rows of segment s are
+ *                      [cu_seqlens_q[s], cu_seqlens_q[s+1]) of the flattened
+ *                      [batch * q_len] rows; 0 .. batch*q_len, increasing.
+ *   cu_seqlens_k[n+1]  prefix sums of segment key counts (non-decreasing; a
+ *                      padding segment adds 0).
+ *   seg_k_begin[n]     flattened key index (b * seq_len + position) of the
+ *                      segment's first key; for a padding segment, the
+ *                      position of its first row.
+ *   *n_seg, *max_seqlen_q, *max_seqlen_k.
+ * Row t of segment s (0-based) attends keys seg_k_begin[s] + 0 ..
+ * seg_k_begin[s] + t + (k_len - q_len) inclusive (bottom-right alignment).
+ * Errors: BD_ERR_INVALID_ARG (null pointer, bad sizes), BD_ERR_BAD_METADATA
+ * (negative length, row sum > seq_len), BD_ERR_CAPACITY (*n_seg is set to the
+ * number of segments needed; nothing else is written).  The table is checked
+ * with blockdiag_validate before returning.
+ */
+bd_status blockdiag_segment(const int32_t *doc_lens, const int32_t *docs_per_row,
+                            int32_t batch, int32_t seq_len, int32_t row_offset,
+                            int32_t q_len, int32_t capacity, int32_t *cu_seqlens_q,
+                            int32_t *cu_seqlens_k, int32_t *seg_k_begin, int32_t *n_seg,
+                            int32_t *max_seqlen_q, int32_t *max_seqlen_k);
+
+/*
+ * blockdiag_validate -- host check of a segment table built anywhere (Design
+ * overview, kernels.py, and key property 4: every offset a kernel consumes is
+ * validated on the host, since a bad terminal offset would otherwise be an
+ * asynchronous illegal memory access).  Host pointers.  Checks: cu_q[0] = 0,
+ * strictly increasing, cu_q[n] = batch * q_len; cu_k[0] = 0, non-decreasing;
+ * each segment's rows lie in one batch row; a non-padding segment's keys lie
+ * in the same batch row, number at least its rows, and end exactly one past
+ * the global position of its last row; padding segments have no keys and
+ * only follow the row's last document; segments of a row are contiguous and
+ * in order.  Returns BD_OK or BD_ERR_BAD_METADATA with a message.
+ */
+bd_status blockdiag_validate(const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                             const int32_t *seg_k_begin, int32_t n_seg, int32_t batch,
+                             int32_t seq_len, int32_t row_offset, int32_t q_len);
+
+/*
+ * blockdiag_meta_ints -- number of int32 in the device metadata buffer that
+ * blockdiag_meta_build fills: 2 * batch * q_len + 2 * batch * seq_len.
+ *
+ * blockdiag_meta_build -- expands a validated segment table (device copy)
+ * into per-row and per-key mask bounds on the device, once per step, so the
+ * attention kernels find each tile's live key range, each key tile's live
+ * query range and every element's mask with plain loads (skipping fully
+ * masked tiles, Summary: per-step precompute, zero per-layer host syncs).
+ *   d_table   device int32 [3 * n_seg + 2] = cu_seqlens_q[n_seg+1] ++
+ *             cu_seqlens_k[n_seg+1] ++ seg_k_begin[n_seg], as produced by
+ *             blockdiag_segment and accepted by blockdiag_validate.
+ *   d_meta    device int32 [blockdiag_meta_ints(...)], written as
+ *             row_lo[batch][q_len], row_hi[batch][q_len]: local row t of
+ *               batch row b attends key positions row_lo <= j < row_hi
+ *               (row_lo = row_hi = 0 on padding rows);
+ *             key_qlo[batch][seq_len], key_qhi[batch][seq_len]: key position
+ *               j of row b is attended by local rows key_qlo <= t < key_qhi
+ *               (both 0 when no local row attends it).
+ * The table is not re-validated here (that needs a sync); the kernel clamps
+ * every bound to its row so a corrupt table cannot make later kernels read
+ * out of bounds.  Errors: BD_ERR_INVALID_ARG, BD_ERR_HIP.
+ */
+size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_len);
+bd_status blockdiag_meta_build(const int32_t *d_table, int32_t n_seg, int32_t batch,
+                               int32_t seq_len, int32_t row_offset, int32_t q_len,
+                               int32_t *d_meta, void *stream);
+
+/*
+ * blockdiag_workspace_bytes -- device scratch the forward (is_bwd = 0) or
+ * backward (is_bwd = 1) needs for these sizes (0 is a valid answer).
+ */
+size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int32_t seq_len,
+                                 int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim);
+
+/*
+ * blockdiag_attn_fwd -- O and LSE of the chunk (Summary: the varlen kernel;
+ * Design overview, runtime.py: drop-in SDPA; packed.py: row_offset = 0).
+ *   q, k, v (device, dtype) as in the conventions above; d_meta (device) from
+ *   blockdiag_meta_build for the same batch/seq_len/row_offset/q_len; o
+ *   (device, dtype) and lse (device, float32) are written in full.
+ *   scale multiplies q.k (1/sqrt(head_dim) is the usual choice).
+ *   Supported: head_dim in {64, 128} for both dtypes, any other head_dim up
+ *   to 256 that is a multiple of 8 through the generic kernel; h_q % h_kv = 0.
+ *   bf16 inputs are multiplied on matrix cores with float32 accumulation; the
+ *   outputs are rounded to nearest even.  The forward is bitwise
+ *   deterministic (no atomics), so a replayed forward equals the original.
+ * q_len = 0 or batch = 0 is a no-op returning BD_OK.
+ * Errors: BD_ERR_INVALID_ARG, BD_ERR_UNSUPPORTED, BD_ERR_WORKSPACE, BD_ERR_HIP.
+ */
+bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
+                             int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                             float scale, const void *q, const void *k, const void *v,
+                             const int32_t *d_meta, void *o, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * blockdiag_attn_bwd -- dQ, dK, dV of the loss sum(dO * O) for the chunk
+ * (Proof section: forward/backward parity and input gradients).  LSE has no
+ * incoming gradient.  o and lse are the forward's outputs; d_o like o.
+ *   dq (device, like q) is written in full; dk, dv (device, like k) are
+ *   written for every key of every row -- the chunk's partial gradients, zero
+ *   at keys no local row attends, so summing them over the chunks of a row
+ *   gives the full gradient (Design overview, exchange.py: the K/V gradient
+ *   is reduce-scattered with SUM).
+ *   workspace: at least blockdiag_workspace_bytes(1, ...) bytes of device
+ *   memory (float32 row statistics and a float32 dQ accumulator).
+ * The dK/dV result is deterministic; dQ is accumulated with float32 atomics
+ * on matrix-core paths, so its last bits may differ run to run.
+ * Errors: as blockdiag_attn_fwd.
+ */
+bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
+                             int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                             float scale, const void *q, const void *k, const void *v,
+                             const void *o, const float *lse, const void *d_o,
+                             const int32_t *d_meta, void *dq, void *dk, void *dv,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char *blockdiag_last_error(void);
+
+/* Library version string. */
+const char *blockdiag_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKDIAG_H */

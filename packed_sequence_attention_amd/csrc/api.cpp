@@ -1,0 +1,137 @@
+// C ABI of the block-diagonal packed attention library: argument checks,
+// workspace sizing and dispatch to the gfx950 kernels.  Every check runs on
+// the host before anything is enqueued (Automodel page "feat(distributed):
+// block-diagonal varlen CP for packed sequences", key property 4: kernel
+// inputs are validated on the host so a bad offset raises instead of
+// faulting asynchronously).
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+
+#include "../../include/blockdiag.h"
+#include "internal.h"
+#include "launch.h"
+
+using bd::fail;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+
+bd_status check_common(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
+                       int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim, float scale) {
+  if (dtype != BD_F32 && dtype != BD_BF16) return fail(BD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+  if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0)
+    return fail(BD_ERR_INVALID_ARG, "negative size");
+  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
+    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
+  if (h_q <= 0 || h_kv <= 0 || h_q % h_kv != 0)
+    return fail(BD_ERR_INVALID_ARG, "h_q (%d) must be a positive multiple of h_kv (%d)", h_q, h_kv);
+  if (head_dim <= 0 || head_dim > 256 || head_dim % 8 != 0)
+    return fail(BD_ERR_UNSUPPORTED, "head_dim %d: supported are multiples of 8 up to 256", head_dim);
+  if (!isfinite(scale)) return fail(BD_ERR_INVALID_ARG, "scale must be finite");
+  const int64_t nq = static_cast<int64_t>(batch) * q_len * h_q * head_dim;
+  const int64_t nk = static_cast<int64_t>(batch) * seq_len * h_kv * head_dim;
+  if (nq > kMaxElems || nk > kMaxElems || static_cast<int64_t>(batch) * seq_len > kMaxElems)
+    return fail(BD_ERR_INVALID_ARG, "tensor too large for 32-bit element counts");
+  return BD_OK;
+}
+
+bool use_mfma(bd_dtype dtype, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
+  return bd::mfma_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+
+extern "C" size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_len) {
+  if (batch < 0 || seq_len < 0 || q_len < 0) return 0;
+  return 2 * static_cast<size_t>(batch) * q_len + 2 * static_cast<size_t>(batch) * seq_len;
+}
+
+extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, int32_t n_seg, int32_t batch,
+                                          int32_t seq_len, int32_t row_offset, int32_t q_len,
+                                          int32_t* d_meta, void* stream) {
+  bd::clear_error();
+  if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0 || n_seg < 0)
+    return fail(BD_ERR_INVALID_ARG, "negative size");
+  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
+    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
+  if (static_cast<int64_t>(batch) * seq_len > kMaxElems) return fail(BD_ERR_INVALID_ARG, "too large");
+  if (blockdiag_meta_ints(batch, seq_len, q_len) == 0) return BD_OK;
+  if (d_table == nullptr || d_meta == nullptr) return fail(BD_ERR_INVALID_ARG, "null pointer");
+  if (n_seg == 0 && static_cast<int64_t>(batch) * q_len > 0)
+    return fail(BD_ERR_BAD_METADATA, "empty segment table for a non-empty chunk");
+  hipError_t e = bd::launch_meta_build(d_table, n_seg, batch, seq_len, row_offset, q_len, d_meta,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
+  return BD_OK;
+}
+
+extern "C" size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int32_t seq_len,
+                                            int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim) {
+  (void)seq_len;
+  if (!is_bwd || batch <= 0 || q_len <= 0 || h_q <= 0 || head_dim <= 0) return 0;
+  const size_t rows = static_cast<size_t>(batch) * q_len * h_q;
+  size_t bytes = align256(rows * sizeof(float));  // delta
+  if (use_mfma(dtype, head_dim, h_q, h_kv, 1.f)) bytes += align256(rows * head_dim * sizeof(float));
+  return bytes;
+}
+
+extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
+                                        int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                                        float scale, const void* q, const void* k, const void* v,
+                                        const int32_t* d_meta, void* o, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  bd::clear_error();
+  (void)workspace;
+  bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale);
+  if (st != BD_OK) return st;
+  if (batch == 0 || q_len == 0) return BD_OK;
+  if (!q || !k || !v || !d_meta || !o || !lse) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
+  const size_t need = blockdiag_workspace_bytes(0, dtype, batch, seq_len, q_len, h_q, h_kv, head_dim);
+  if (workspace_bytes < need) return fail(BD_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  bd::FwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
+                q, k, v, d_meta, o, lse};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = use_mfma(dtype, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
+                                                             : bd::launch_fwd_generic(a, s);
+  if (e != hipSuccess) return fail(BD_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return BD_OK;
+}
+
+extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
+                                        int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                                        float scale, const void* q, const void* k, const void* v,
+                                        const void* o, const float* lse, const void* d_o,
+                                        const int32_t* d_meta, void* dq, void* dk, void* dv,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  bd::clear_error();
+  bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale);
+  if (st != BD_OK) return st;
+  if (batch == 0) return BD_OK;
+  if (!k || !v || !d_meta || !dk || !dv) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
+  if (q_len > 0 && (!q || !o || !lse || !d_o || !dq)) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
+  const size_t need = blockdiag_workspace_bytes(1, dtype, batch, seq_len, q_len, h_q, h_kv, head_dim);
+  if (workspace_bytes < need) return fail(BD_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (need > 0 && workspace == nullptr) return fail(BD_ERR_WORKSPACE, "null workspace");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (q_len == 0) {
+    // No local rows: the chunk's partial dK/dV are zero.
+    const int64_t words = static_cast<int64_t>(batch) * seq_len * h_kv * head_dim * (dtype == BD_F32 ? 2 : 1);
+    hipError_t e = bd::launch_zero_u16(dk, words, s);
+    if (e == hipSuccess) e = bd::launch_zero_u16(dv, words, s);
+    if (e != hipSuccess) return fail(BD_ERR_HIP, "zero-fill: %s", hipGetErrorString(e));
+    return BD_OK;
+  }
+  const size_t rows = static_cast<size_t>(batch) * q_len * h_q;
+  char* ws = static_cast<char*>(workspace);
+  const bool mf = use_mfma(dtype, head_dim, h_q, h_kv, scale);
+  bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
+                q, k, v, o, lse, d_o, d_meta, dq, dk, dv,
+                reinterpret_cast<float*>(ws),
+                mf ? reinterpret_cast<float*>(ws + align256(rows * sizeof(float))) : nullptr};
+  hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);
+  if (e != hipSuccess) return fail(BD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return BD_OK;
+}

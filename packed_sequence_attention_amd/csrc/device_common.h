@@ -1,0 +1,96 @@
+// Device-side helpers shared by the gfx950 kernels of the block-diagonal
+// packed attention library: vector types for the bf16 matrix-core
+// instructions, bf16 <-> f32 conversion, wave reductions and the launch
+// parameter blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Raw bf16 bits <-> float.  bf16 -> f32 is exact; f32 -> bf16 rounds to
+// nearest even in hardware (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 h = static_cast<__bf16>(x);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Element loads/stores for the generic kernels (float or raw bf16 bits).
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Launch parameters.  Sizes are int32 (checked on the host); element
+// offsets are computed in 64-bit.
+struct AttnShape {
+  int batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, group;
+  float scale;
+};
+
+struct MetaView {
+  const int32_t* row_lo;   // [batch][q_len]
+  const int32_t* row_hi;   // [batch][q_len]
+  const int32_t* key_qlo;  // [batch][seq_len]
+  const int32_t* key_qhi;  // [batch][seq_len]
+};
+
+__host__ __device__ inline MetaView meta_view(const int32_t* meta, int batch, int seq_len, int q_len) {
+  const int64_t nr = static_cast<int64_t>(batch) * q_len;
+  const int64_t nk = static_cast<int64_t>(batch) * seq_len;
+  MetaView m;
+  m.row_lo = meta;
+  m.row_hi = meta + nr;
+  m.key_qlo = meta + 2 * nr;
+  m.key_qhi = meta + 2 * nr + nk;
+  return m;
+}
+
+}  // namespace bd

@@ -1,0 +1,249 @@
+// bf16 matrix-core forward of block-diagonal packed attention for gfx950.
+//
+// Automodel page "feat(distributed): block-diagonal varlen CP for packed
+// sequences": Summary (varlen attention over packed documents, block-causal
+// per document) and Design overview (one GPU's contiguous query chunk against
+// the whole row's K/V).  The online softmax (running max, running sum,
+// rescaled accumulator) is the standard streaming form of softmax attention.
+//
+// Work decomposition (one workgroup = 4 waves):
+//   workgroup = (batch row b, 4 query heads sharing one K/V head, 32 local
+//   query rows); wave w owns query head 4*hg + w for those 32 rows, so all
+//   four waves share every K/V tile staged in LDS (grouped-query reuse) and
+//   have the same live key range.
+//   Key tiles are 64 keys anchored at multiples of 64 in the row; only tiles
+//   in [doc_start(first real row), last real row] are visited (every one of
+//   them holds an allowed pair), and the element mask is applied only on
+//   tiles that are not entirely allowed.
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16, lane l, n = l % 32,
+// kg = l / 32):
+//   S^T = K Q^T per 32-key block: A = K rows from LDS, B = the wave's Q rows
+//   held in registers; accumulator element j is key (j/4)*8 + kg*4 + j%4,
+//   query n, so each lane owns one query row and its softmax statistics stay
+//   in the lane (the two lanes of a row exchange one value per block).
+//   O^T += V^T P^T: B = P straight from the accumulator (bf16), A = V^T read
+//   with the LDS transpose load (ds_read_b64_tr_b16) from row-major V, with
+//   the key order of the accumulator; O^T accumulates in registers.
+// Softmax in base 2 with scale*log2(e) folded in; the running max is only
+// raised when it grows by more than 8 (a factor 256), which keeps every
+// exponent <= 2^8 and skips most accumulator rescales; the result is the
+// same function since numerator and denominator share the reference.
+#include <limits.h>
+#include <math.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bd {
+namespace {
+
+constexpr int kBN = 64;  // keys per tile
+constexpr int kBM = 32;  // query rows per workgroup (one per lane pair)
+
+template <int D>
+struct FwdLds {
+  static constexpr int KP = D * 2 + 16;  // K row pitch (bytes): 16-byte skew per row
+  static constexpr int VP = D * 2 + 64;  // V row pitch: rows of a transpose read hit distinct banks
+  static constexpr int bytes = kBN * (KP + VP);
+};
+
+__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, int second_off) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + second_off));
+  const auto ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, MetaView m,
+                                                          uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse, int n_qt, int n_hg) {
+  constexpr int KK = D / 16;  // k-steps of Q K^T
+  constexpr int DB = D / 32;  // 32-wide blocks of O^T
+  constexpr int KP = FwdLds<D>::KP;
+  constexpr int VP = FwdLds<D>::VP;
+  constexpr int CH = D / 8;   // 16-byte chunks per K/V row
+  __shared__ __attribute__((aligned(16))) char smem[FwdLds<D>::bytes];
+  char* sK = smem;
+  char* sV = smem + kBN * KP;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, kg = lane >> 5;
+
+  // Longest-first: the last query tiles of a row have the longest key ranges.
+  const int per_qt = s.batch * n_hg;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+  const int rem = static_cast<int>(blockIdx.x) % per_qt;
+  const int b = rem / n_hg, hg = rem % n_hg;
+  const int h = hg * 4 + wave;
+  const int g = (hg * 4) / s.group;
+
+  const int t = qt * kBM + n;
+  const bool valid = t < s.q_len;
+  const int64_t bt = static_cast<int64_t>(b) * s.q_len + t;
+  int lo = 0, hi = 0;
+  if (valid) {
+    lo = m.row_lo[bt];
+    hi = m.row_hi[bt];
+  }
+  const bool real = hi > lo;
+  const int kmin = wave_min_i(real ? lo : INT_MAX);
+  const int kmax = wave_max_i(real ? hi : 0);
+  const int lomax = wave_max_i(real ? lo : 0);
+  const bool all_real = wave_min_i(real ? 1 : 0) == 1;
+  const int pfirst = s.row_offset + qt * kBM;
+
+  bf16x8 qf[KK];
+  {
+    const uint16_t* qrow = q + (bt * s.h_q + h) * D + kg * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (valid) {
+        qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(0.f);
+      }
+    }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+  const float c = s.scale * kLog2e;
+
+  // Per-lane LDS offsets.
+  const int k_rd = n * KP + kg * 16;
+  const int v_rd = (4 * kg + ((lane & 15) >> 2)) * VP + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+
+  if (kmax > kmin) {
+    const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
+    for (int kt = kt0; kt <= kt1; ++kt) {
+      const int k0 = kt * kBN;
+      __syncthreads();
+      for (int ci = tid; ci < kBN * CH; ci += 256) {
+        const int r = ci / CH, col = ci % CH;
+        const int j = k0 + r;
+        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+        if (j < s.seq_len) {
+          const int64_t off = ((static_cast<int64_t>(b) * s.seq_len + j) * s.h_kv + g) * D + col * 8;
+          kx = *reinterpret_cast<const uint4*>(k + off);
+          vx = *reinterpret_cast<const uint4*>(v + off);
+        }
+        *reinterpret_cast<uint4*>(sK + r * KP + col * 16) = kx;
+        *reinterpret_cast<uint4*>(sV + r * VP + col * 16) = vx;
+      }
+      __syncthreads();
+      const bool full = all_real && lomax <= k0 && k0 + kBN - 1 <= pfirst;
+#pragma unroll
+      for (int sb = 0; sb < kBN / 32; ++sb) {
+        f32x16 sacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + sb * 32 * KP + k_rd + kk * 32);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
+        }
+        if (!full) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + sb * 32 + (j >> 2) * 8 + kg * 4 + (j & 3);
+            if (key < lo || key >= hi) sacc[j] = -INFINITY;
+          }
+        }
+        float mx = sacc[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrun, mx * c);
+        const bool need = mnew > mrun + 8.f;
+        if (__any(need)) {
+          const float alpha = need ? exp2f(mrun - mnew) : 1.f;
+          if (need) mrun = mnew;
+          lrun *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
+        }
+        const float mu = (mrun == -INFINITY) ? 0.f : mrun;
+        float p[16];
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -mu));
+          ps += p[j];
+        }
+        lrun += ps;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pb[0][i] = static_cast<__bf16>(p[i]);
+          pb[1][i] = static_cast<__bf16>(p[8 + i]);
+        }
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const char* vb = sV + (sb * 32 + 16 * kk2) * VP + v_rd;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 va = lds_tr_pair(vb + db * 64, 8 * VP);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk2], oacc[db], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+  if (valid) {
+    const bool any = ltot > 0.f;
+    const float inv = any ? 1.f / ltot : 0.f;
+    uint16_t* orow = o + (bt * s.h_q + h) * D + kg * 4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        uint2 pk;
+        pk.x = pack_bf16x2(oacc[db][4 * jq] * inv, oacc[db][4 * jq + 1] * inv);
+        pk.y = pack_bf16x2(oacc[db][4 * jq + 2] * inv, oacc[db][4 * jq + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + db * 32 + jq * 8) = pk;
+      }
+    if (kg == 0)
+      lse[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t] =
+          any ? fmaf(mrun, kLn2, logf(ltot)) : -INFINITY;
+  }
+}
+
+template <int D>
+hipError_t fwd_mfma_t(const FwdArgs& a, hipStream_t st) {
+  AttnShape s;
+  s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
+  s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
+  MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
+  const int n_qt = (a.q_len + kBM - 1) / kBM;
+  const int n_hg = a.h_q / 4;
+  const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
+  fwd_mfma_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
+      s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+      static_cast<const uint16_t*>(a.v), m, static_cast<uint16_t*>(a.o), a.lse, n_qt, n_hg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv) {
+  return dtype == 1 && (head_dim == 64 || head_dim == 128) && h_kv > 0 && h_q % h_kv == 0 &&
+         (h_q / h_kv) % 4 == 0;
+}
+
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
+  return a.head_dim == 64 ? fwd_mfma_t<64>(a, st) : fwd_mfma_t<128>(a, st);
+}
+
+}  // namespace bd

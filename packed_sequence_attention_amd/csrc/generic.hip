@@ -1,0 +1,386 @@
+// Generic (vector-ALU) kernels of block-diagonal packed attention: float32
+// or bfloat16 tensors, any head_dim up to 256 that is a multiple of 8, any
+// grouped-query ratio.  They serve the float32 path and the shapes the
+// matrix-core kernels do not cover.  All arithmetic is float32.
+//
+// Automodel page "feat(distributed): block-diagonal varlen CP for packed
+// sequences": Summary/Motivation (block-causal attention per document, the
+// same function as a dense masked SDPA) and the Proof section (forward and
+// input gradients).  Each local row visits exactly the keys of its own
+// document up to itself ([row_lo, row_hi) from the per-step metadata); each
+// key visits exactly the local rows attending it ([key_qlo, key_qhi)), so no
+// fully masked work is done and no atomics are needed.
+//
+// Backward uses the row statistic delta_i = sum_d dO_i O_i (equal to
+// sum_j P_ij dP_ij), computed once by the preparation kernel.
+#include <math.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bd {
+namespace {
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Load 8 consecutive elements as float.
+__device__ __forceinline__ void load8(const float* p, float out[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float out[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// dot(x_lds[0:D], row[0:D]) with the row read from global memory.
+template <typename T>
+__device__ __forceinline__ float dot_row(const float* x_lds, const T* row, int D) {
+  float acc = 0.f;
+  for (int d = 0; d < D; d += 8) {
+    float r[8];
+    load8(row + d, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(x_lds[d + e], r[e], acc);
+  }
+  return acc;
+}
+
+constexpr int kWaves = 4;
+constexpr int kMaxD = 256;
+
+// One wave per (b, query head, local row).
+template <typename T, int NR>
+__global__ __launch_bounds__(256) void fwd_generic_kernel(AttnShape s, const T* __restrict__ q,
+                                                          const T* __restrict__ k,
+                                                          const T* __restrict__ v, MetaView m,
+                                                          T* __restrict__ o, float* __restrict__ lse) {
+  __shared__ float sq[kWaves][kMaxD];
+  __shared__ float sp[kWaves][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t total = static_cast<int64_t>(s.batch) * s.q_len * s.h_q;
+  if (w >= total) return;  // no block-wide barrier below: waves are independent
+  const int D = s.head_dim;
+  const int h = static_cast<int>(w % s.h_q);
+  const int64_t bt = w / s.h_q;
+  const int t = static_cast<int>(bt % s.q_len);
+  const int b = static_cast<int>(bt / s.q_len);
+  const int g = h / s.group;
+  const T* qrow = q + (bt * s.h_q + h) * D;
+  for (int d = lane; d < D; d += 64) sq[wave][d] = Elem<T>::load(qrow + d);
+  wave_sync();
+  const int lo = m.row_lo[bt], hi = m.row_hi[bt];
+  const int64_t kv_base = static_cast<int64_t>(b) * s.seq_len;
+  float mrun = -INFINITY, lrun = 0.f, acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+  for (int j0 = lo; j0 < hi; j0 += 64) {
+    const int j = j0 + lane;
+    float sc = -INFINITY;
+    if (j < hi) sc = s.scale * dot_row(sq[wave], k + ((kv_base + j) * s.h_kv + g) * D, D);
+    const float mnew = fmaxf(mrun, wave_max(sc));  // finite: lane 0 is in range
+    const float p = (j < hi) ? expf(sc - mnew) : 0.f;
+    const float alpha = expf(mrun - mnew);
+    lrun = lrun * alpha + wave_sum(p);
+    sp[wave][lane] = p;
+    wave_sync();
+    const int n = min(64, hi - j0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] *= alpha;
+    for (int jj = 0; jj < n; ++jj) {
+      const float pj = sp[wave][jj];
+      const T* vrow = v + ((kv_base + j0 + jj) * s.h_kv + g) * D;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int d = lane + 64 * r;
+        if (d < D) acc[r] = fmaf(pj, Elem<T>::load(vrow + d), acc[r]);
+      }
+    }
+    mrun = mnew;
+    wave_sync();
+  }
+  const bool any = hi > lo;
+  const float inv = any ? 1.f / lrun : 0.f;
+  T* orow = o + (bt * s.h_q + h) * D;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int d = lane + 64 * r;
+    if (d < D) Elem<T>::store(orow + d, acc[r] * inv);
+  }
+  if (lane == 0)
+    lse[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t] = any ? mrun + logf(lrun) : -INFINITY;
+}
+
+// One wave per (b, query head, local row): dQ_i = scale * sum_j dS_ij k_j.
+template <typename T, int NR>
+__global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* __restrict__ q,
+                                                         const T* __restrict__ k,
+                                                         const T* __restrict__ v,
+                                                         const T* __restrict__ d_o,
+                                                         const float* __restrict__ lse,
+                                                         const float* __restrict__ delta, MetaView m,
+                                                         T* __restrict__ dq) {
+  __shared__ float sq[kWaves][kMaxD];
+  __shared__ float sdo[kWaves][kMaxD];
+  __shared__ float sp[kWaves][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t total = static_cast<int64_t>(s.batch) * s.q_len * s.h_q;
+  if (w >= total) return;
+  const int D = s.head_dim;
+  const int h = static_cast<int>(w % s.h_q);
+  const int64_t bt = w / s.h_q;
+  const int t = static_cast<int>(bt % s.q_len);
+  const int b = static_cast<int>(bt / s.q_len);
+  const int g = h / s.group;
+  const int64_t row = (bt * s.h_q + h) * D;
+  for (int d = lane; d < D; d += 64) {
+    sq[wave][d] = Elem<T>::load(q + row + d);
+    sdo[wave][d] = Elem<T>::load(d_o + row + d);
+  }
+  wave_sync();
+  const int lo = m.row_lo[bt], hi = m.row_hi[bt];
+  const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
+  const float lse_t = hi > lo ? lse[st] : 0.f;
+  const float delta_t = delta[st];
+  const int64_t kv_base = static_cast<int64_t>(b) * s.seq_len;
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+  for (int j0 = lo; j0 < hi; j0 += 64) {
+    const int j = j0 + lane;
+    float ds = 0.f;
+    if (j < hi) {
+      const int64_t kr = ((kv_base + j) * s.h_kv + g) * D;
+      const float p = expf(s.scale * dot_row(sq[wave], k + kr, D) - lse_t);
+      const float dp = dot_row(sdo[wave], v + kr, D);
+      ds = p * (dp - delta_t);
+    }
+    sp[wave][lane] = ds;
+    wave_sync();
+    const int n = min(64, hi - j0);
+    for (int jj = 0; jj < n; ++jj) {
+      const float dsj = sp[wave][jj];
+      const T* krow = k + ((kv_base + j0 + jj) * s.h_kv + g) * D;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int d = lane + 64 * r;
+        if (d < D) acc[r] = fmaf(dsj, Elem<T>::load(krow + d), acc[r]);
+      }
+    }
+    wave_sync();
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int d = lane + 64 * r;
+    if (d < D) Elem<T>::store(dq + row + d, acc[r] * s.scale);
+  }
+}
+
+// One wave per (b, K/V head, key position): dV_j = sum_i P_ij dO_i and
+// dK_j = scale * sum_i dS_ij q_i over the group's query heads and the local
+// rows attending j.  Keys no row attends get zeros.
+template <typename T, int NR>
+__global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* __restrict__ q,
+                                                          const T* __restrict__ k,
+                                                          const T* __restrict__ v,
+                                                          const T* __restrict__ d_o,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ delta, MetaView m,
+                                                          T* __restrict__ dk, T* __restrict__ dv) {
+  __shared__ float sk[kWaves][kMaxD];
+  __shared__ float sv[kWaves][kMaxD];
+  __shared__ float sp[kWaves][64];
+  __shared__ float sds[kWaves][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t total = static_cast<int64_t>(s.batch) * s.seq_len * s.h_kv;
+  if (w >= total) return;
+  const int D = s.head_dim;
+  const int g = static_cast<int>(w % s.h_kv);
+  const int64_t bj = w / s.h_kv;
+  const int b = static_cast<int>(bj / s.seq_len);
+  const int64_t krow = (bj * s.h_kv + g) * D;
+  for (int d = lane; d < D; d += 64) {
+    sk[wave][d] = Elem<T>::load(k + krow + d);
+    sv[wave][d] = Elem<T>::load(v + krow + d);
+  }
+  wave_sync();
+  const int qlo = m.key_qlo[bj], qhi = m.key_qhi[bj];
+  float adk[NR], adv[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) adk[r] = adv[r] = 0.f;
+  for (int hh = 0; hh < s.group; ++hh) {
+    const int h = g * s.group + hh;
+    for (int t0 = qlo; t0 < qhi; t0 += 64) {
+      const int t = t0 + lane;
+      float p = 0.f, ds = 0.f;
+      if (t < qhi) {
+        const int64_t row = ((static_cast<int64_t>(b) * s.q_len + t) * s.h_q + h) * D;
+        const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
+        p = expf(s.scale * dot_row(sk[wave], q + row, D) - lse[st]);
+        const float dp = dot_row(sv[wave], d_o + row, D);
+        ds = p * (dp - delta[st]);
+      }
+      sp[wave][lane] = p;
+      sds[wave][lane] = ds;
+      wave_sync();
+      const int n = min(64, qhi - t0);
+      for (int tt = 0; tt < n; ++tt) {
+        const float pt = sp[wave][tt], dst = sds[wave][tt];
+        const int64_t row = ((static_cast<int64_t>(b) * s.q_len + t0 + tt) * s.h_q + h) * D;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int d = lane + 64 * r;
+          if (d < D) {
+            adv[r] = fmaf(pt, Elem<T>::load(d_o + row + d), adv[r]);
+            adk[r] = fmaf(dst, Elem<T>::load(q + row + d), adk[r]);
+          }
+        }
+      }
+      wave_sync();
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int d = lane + 64 * r;
+    if (d < D) {
+      Elem<T>::store(dk + krow + d, adk[r] * s.scale);
+      Elem<T>::store(dv + krow + d, adv[r]);
+    }
+  }
+}
+
+// One thread per (b, local row, query head): delta = sum_d dO * O in float32;
+// also zeroes that row of the float32 dQ accumulator when one is given.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(AttnShape s, const T* __restrict__ o,
+                                                       const T* __restrict__ d_o,
+                                                       float* __restrict__ delta,
+                                                       float* __restrict__ dq_acc) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(s.batch) * s.q_len * s.h_q;
+  if (idx >= total) return;
+  const int D = s.head_dim;
+  const int h = static_cast<int>(idx % s.h_q);
+  const int64_t bt = idx / s.h_q;
+  const int t = static_cast<int>(bt % s.q_len);
+  const int b = static_cast<int>(bt / s.q_len);
+  const int64_t row = idx * D;
+  float acc = 0.f;
+  for (int d = 0; d < D; d += 8) {
+    float x[8], y[8];
+    load8(o + row + d, x);
+    load8(d_o + row + d, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
+  }
+  delta[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t] = acc;
+  if (dq_acc != nullptr) {
+    float4* z = reinterpret_cast<float4*>(dq_acc + row);
+    for (int d = 0; d < D / 4; ++d) z[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+AttnShape make_shape(int batch, int seq_len, int row_offset, int q_len, int h_q, int h_kv,
+                     int head_dim, float scale) {
+  AttnShape s;
+  s.batch = batch; s.seq_len = seq_len; s.row_offset = row_offset; s.q_len = q_len;
+  s.h_q = h_q; s.h_kv = h_kv; s.head_dim = head_dim; s.group = h_q / h_kv; s.scale = scale;
+  return s;
+}
+
+unsigned blocks_for(int64_t waves) { return static_cast<unsigned>((waves + kWaves - 1) / kWaves); }
+
+template <typename T, int NR>
+hipError_t fwd_generic_t(const FwdArgs& a, hipStream_t st) {
+  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
+  MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
+  const int64_t waves = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
+  fwd_generic_kernel<T, NR><<<blocks_for(waves), 256, 0, st>>>(
+      s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), m,
+      static_cast<T*>(a.o), a.lse);
+  return hipGetLastError();
+}
+
+template <typename T, int NR>
+hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
+  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
+  MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
+  bwd_prep_kernel<T><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, st>>>(
+      s, static_cast<const T*>(a.o), static_cast<const T*>(a.d_o), a.delta, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dq_generic_kernel<T, NR><<<blocks_for(rows), 256, 0, st>>>(
+      s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+      static_cast<const T*>(a.d_o), a.lse, a.delta, m, static_cast<T*>(a.dq));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t keys = static_cast<int64_t>(a.batch) * a.seq_len * a.h_kv;
+  dkv_generic_kernel<T, NR><<<blocks_for(keys), 256, 0, st>>>(
+      s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+      static_cast<const T*>(a.d_o), a.lse, a.delta, m, static_cast<T*>(a.dk),
+      static_cast<T*>(a.dv));
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t fwd_generic_d(const FwdArgs& a, hipStream_t st) {
+  if (a.head_dim <= 64) return fwd_generic_t<T, 1>(a, st);
+  if (a.head_dim <= 128) return fwd_generic_t<T, 2>(a, st);
+  return fwd_generic_t<T, 4>(a, st);
+}
+template <typename T>
+hipError_t bwd_generic_d(const BwdArgs& a, hipStream_t st) {
+  if (a.head_dim <= 64) return bwd_generic_t<T, 1>(a, st);
+  if (a.head_dim <= 128) return bwd_generic_t<T, 2>(a, st);
+  return bwd_generic_t<T, 4>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_generic(const FwdArgs& a, hipStream_t st) {
+  return a.dtype == 0 ? fwd_generic_d<float>(a, st) : fwd_generic_d<uint16_t>(a, st);
+}
+
+hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t st) {
+  return a.dtype == 0 ? bwd_generic_d<float>(a, st) : bwd_generic_d<uint16_t>(a, st);
+}
+
+__global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t* __restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_u16(void* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  zero_u16_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), 256, 0, st>>>(static_cast<uint16_t*>(p), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
+  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
+  const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
+  if (a.dtype == 0)
+    bwd_prep_kernel<float><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, st>>>(
+        s, static_cast<const float*>(a.o), static_cast<const float*>(a.d_o), a.delta, a.dq_acc);
+  else
+    bwd_prep_kernel<uint16_t><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, st>>>(
+        s, static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.d_o), a.delta, a.dq_acc);
+  return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,62 @@
+// Host-side launch functions of the gfx950 kernels, called by the C ABI
+// layer (api.cpp) after every argument has been checked.  Each returns the
+// hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bd {
+
+struct FwdArgs {
+  int dtype;  // 0 = f32, 1 = bf16
+  int batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* meta;
+  void* o;
+  float* lse;
+};
+
+struct BwdArgs {
+  int dtype;
+  int batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* d_o;
+  const int32_t* meta;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;   // workspace: [batch][h_q][q_len]
+  float* dq_acc;  // workspace: [batch][q_len][h_q][head_dim] (matrix-core path only)
+};
+
+// Metadata expansion (segment table -> per-row / per-key bounds).
+hipError_t launch_meta_build(const int32_t* d_table, int n_seg, int batch, int seq_len,
+                             int row_offset, int q_len, int32_t* d_meta, hipStream_t stream);
+
+// Generic kernels: any head_dim <= 256 that is a multiple of 8, f32 or bf16.
+hipError_t launch_fwd_generic(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t stream);
+
+// bf16 matrix-core kernels: head_dim in {64, 128}, h_q / h_kv a multiple of 4.
+bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv);
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
+
+// Backward row statistics: delta = rowsum(dO * O) in float32, and (if
+// dq_acc is non-null) zero the float32 dQ accumulator.
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
+
+// Fill n 16-bit words with zeros (a kernel, so it is safe under graph capture).
+hipError_t launch_zero_u16(void* p, int64_t n, hipStream_t stream);
+
+}  // namespace bd

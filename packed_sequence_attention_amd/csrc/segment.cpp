@@ -1,0 +1,184 @@
+// Host-only, integer-only varlen segmentation and validation for
+// block-diagonal packed attention (no HIP dependency).
+//
+// Automodel page "feat(distributed): block-diagonal varlen CP for packed
+// sequences":
+//   - Summary: the varlen kernel is driven by per-step precomputed
+//     cu_seqlens (zero per-layer host syncs);
+//   - Design overview, kernels.py: varlen segmentation and host-side
+//     validation of every index a varlen kernel consumes;
+//   - Design overview, batch.py: each rank holds a contiguous slice
+//     [row_offset, row_offset + q_len) of every row;
+//   - key property 2: a document straddling the slice's left edge gives a
+//     first segment with more keys than queries, bottom-right aligned;
+//   - key property 4: a bad terminal offset must be caught on the host.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/blockdiag.h"
+#include "internal.h"
+
+namespace bd {
+
+static thread_local std::string g_last_error;
+
+bd_status fail(bd_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace bd
+
+using bd::fail;
+
+extern "C" const char* blockdiag_last_error(void) { return bd::g_last_error.c_str(); }
+
+extern "C" const char* blockdiag_version(void) { return "blockdiag-gfx950 0.1.0"; }
+
+extern "C" bd_status blockdiag_validate(const int32_t* cu_q, const int32_t* cu_k, const int32_t* kb,
+                                        int32_t n, int32_t batch, int32_t seq_len,
+                                        int32_t row_offset, int32_t q_len) {
+  bd::clear_error();
+  if (n < 0 || batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0)
+    return fail(BD_ERR_INVALID_ARG, "negative size");
+  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
+    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
+  if (cu_q == nullptr || cu_k == nullptr || (n > 0 && kb == nullptr))
+    return fail(BD_ERR_INVALID_ARG, "null table pointer");
+  const int64_t rows = static_cast<int64_t>(batch) * q_len;
+  if (cu_q[0] != 0 || cu_k[0] != 0) return fail(BD_ERR_BAD_METADATA, "cu_seqlens must start at 0");
+  if (cu_q[n] != rows)
+    return fail(BD_ERR_BAD_METADATA, "terminal cu_seqlens_q %d != batch * q_len %lld", cu_q[n],
+                static_cast<long long>(rows));
+  int prev_b = -1;
+  bool prev_padding = false;
+  int64_t prev_key_end = 0;  // row coordinates
+  for (int32_t s = 0; s < n; ++s) {
+    const int64_t q0 = cu_q[s], q1 = cu_q[s + 1];
+    const int64_t qn = q1 - q0, kn = static_cast<int64_t>(cu_k[s + 1]) - cu_k[s];
+    if (qn <= 0) return fail(BD_ERR_BAD_METADATA, "segment %d: cu_seqlens_q not increasing", s);
+    if (kn < 0) return fail(BD_ERR_BAD_METADATA, "segment %d: cu_seqlens_k decreasing", s);
+    const int64_t b = q0 / q_len;
+    if ((q1 - 1) / q_len != b) return fail(BD_ERR_BAD_METADATA, "segment %d spans two batch rows", s);
+    const int64_t p0 = row_offset + (q0 - b * q_len);  // position of the first row
+    const int64_t p_last = p0 + qn - 1;
+    const bool first_of_row = (b != prev_b);
+    if (first_of_row && q0 != b * q_len)
+      return fail(BD_ERR_BAD_METADATA, "segment %d: batch row %lld does not start at its first row", s,
+                  static_cast<long long>(b));
+    if (!first_of_row && prev_padding)
+      return fail(BD_ERR_BAD_METADATA, "segment %d follows a padding segment in the same row", s);
+    const int64_t kbeg = static_cast<int64_t>(kb[s]) - b * seq_len;  // row coordinates
+    if (kn == 0) {
+      if (kbeg != p0)
+        return fail(BD_ERR_BAD_METADATA, "segment %d: padding segment key begin %lld != first row %lld", s,
+                    static_cast<long long>(kbeg), static_cast<long long>(p0));
+      if (q1 != (b + 1) * q_len)
+        return fail(BD_ERR_BAD_METADATA, "segment %d: padding segment does not end the row's chunk", s);
+      if (!first_of_row && prev_key_end != p0)
+        return fail(BD_ERR_BAD_METADATA, "segment %d: gap before padding", s);
+    } else {
+      if (kn < qn) return fail(BD_ERR_BAD_METADATA, "segment %d: fewer keys than queries", s);
+      if (kbeg < 0 || kbeg + kn > seq_len)
+        return fail(BD_ERR_BAD_METADATA, "segment %d: keys outside the batch row", s);
+      if (kbeg + kn != p_last + 1)
+        return fail(BD_ERR_BAD_METADATA, "segment %d: keys do not end at the last row's position", s);
+      if (!first_of_row && (kn != qn || kbeg != prev_key_end))
+        return fail(BD_ERR_BAD_METADATA, "segment %d: only a row's first segment may start left of the chunk", s);
+    }
+    prev_b = static_cast<int>(b);
+    prev_padding = (kn == 0);
+    prev_key_end = kbeg + kn;
+    if (kn == 0) prev_key_end = kbeg;
+  }
+  // Every batch row with rows must have at least one segment (ensured by the
+  // partition: cu_q covers 0 .. batch*q_len without gaps and rows do not
+  // span batch rows).
+  return BD_OK;
+}
+
+extern "C" bd_status blockdiag_segment(const int32_t* doc_lens, const int32_t* docs_per_row,
+                                       int32_t batch, int32_t seq_len, int32_t row_offset,
+                                       int32_t q_len, int32_t capacity, int32_t* cu_q, int32_t* cu_k,
+                                       int32_t* kb, int32_t* n_seg, int32_t* max_q, int32_t* max_k) {
+  bd::clear_error();
+  if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0 || capacity < 0)
+    return fail(BD_ERR_INVALID_ARG, "negative size");
+  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
+    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
+  if (static_cast<int64_t>(batch) * seq_len > INT32_MAX)
+    return fail(BD_ERR_INVALID_ARG, "batch * seq_len exceeds int32");
+  if (n_seg == nullptr || max_q == nullptr || max_k == nullptr || cu_q == nullptr || cu_k == nullptr ||
+      (batch > 0 && docs_per_row == nullptr))
+    return fail(BD_ERR_INVALID_ARG, "null pointer");
+  const int64_t r0 = row_offset, r1 = static_cast<int64_t>(row_offset) + q_len;
+  // Pass 1: check lengths and count segments.
+  int64_t count = 0, di = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (docs_per_row[b] < 0) return fail(BD_ERR_INVALID_ARG, "docs_per_row[%d] < 0", b);
+    if (docs_per_row[b] > 0 && doc_lens == nullptr) return fail(BD_ERR_INVALID_ARG, "null doc_lens");
+    int64_t pos = 0;
+    for (int32_t d = 0; d < docs_per_row[b]; ++d, ++di) {
+      const int64_t L = doc_lens[di];
+      if (L < 0) return fail(BD_ERR_BAD_METADATA, "row %d document %d has negative length", b, d);
+      const int64_t s0 = pos, e0 = pos + L;
+      pos = e0;
+      if (pos > seq_len)
+        return fail(BD_ERR_BAD_METADATA, "row %d: document lengths sum past seq_len %d", b, seq_len);
+      if ((e0 < r1 ? e0 : r1) > (s0 > r0 ? s0 : r0)) ++count;
+    }
+    if ((pos > r0 ? pos : r0) < r1) ++count;  // padding reaches into the chunk
+  }
+  if (count > capacity) {
+    *n_seg = static_cast<int32_t>(count);
+    return fail(BD_ERR_CAPACITY, "segment table needs %lld entries, capacity %d",
+                static_cast<long long>(count), capacity);
+  }
+  if (count > 0 && kb == nullptr) return fail(BD_ERR_INVALID_ARG, "null seg_k_begin");
+  // Pass 2: write.
+  int32_t ns = 0, mq = 0, mk = 0;
+  cu_q[0] = 0;
+  cu_k[0] = 0;
+  di = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    int64_t pos = 0;
+    for (int32_t d = 0; d < docs_per_row[b]; ++d, ++di) {
+      const int64_t s0 = pos, e0 = pos + doc_lens[di];
+      pos = e0;
+      const int64_t qs = s0 > r0 ? s0 : r0, qe = e0 < r1 ? e0 : r1;
+      if (qe <= qs) continue;
+      const int32_t qn = static_cast<int32_t>(qe - qs), kn = static_cast<int32_t>(qe - s0);
+      cu_q[ns + 1] = cu_q[ns] + qn;
+      cu_k[ns + 1] = cu_k[ns] + kn;
+      kb[ns] = static_cast<int32_t>(static_cast<int64_t>(b) * seq_len + s0);
+      mq = qn > mq ? qn : mq;
+      mk = kn > mk ? kn : mk;
+      ++ns;
+    }
+    const int64_t qs = pos > r0 ? pos : r0;
+    if (qs < r1) {
+      const int32_t qn = static_cast<int32_t>(r1 - qs);
+      cu_q[ns + 1] = cu_q[ns] + qn;
+      cu_k[ns + 1] = cu_k[ns];
+      kb[ns] = static_cast<int32_t>(static_cast<int64_t>(b) * seq_len + qs);
+      mq = qn > mq ? qn : mq;
+      ++ns;
+    }
+  }
+  *n_seg = ns;
+  *max_q = mq;
+  *max_k = mk;
+  const bd_status v = blockdiag_validate(cu_q, cu_k, kb, ns, batch, seq_len, row_offset, q_len);
+  if (v != BD_OK) return v;  // unreachable for this construction; kept as a self-check
+  return BD_OK;
+}

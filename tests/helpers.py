@@ -1,0 +1,104 @@
+"""Shared helpers of the GPU parity tests: seeded inputs, calls through the
+C ABI (Python binding), the oracle and the tolerance checks.
+
+Tolerances (float32 workloads / bfloat16 workloads):
+  O:            max-abs <= 1e-5 / 2e-2 (bf16 O: float32 accumulation, output
+                rounded to nearest even)
+  LSE:          max-abs <= 1e-5 / 2e-2
+  dQ, dK, dV:   max-abs <= 1e-4 / relative Frobenius norm <= 5e-2 per tensor
+Segment tables and per-row / per-key bounds: bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import synthetic
+
+TOL = {
+    "f32": {"o": 1e-5, "lse": 1e-5, "grad_abs": 1e-4},
+    "bf16": {"o": 2e-2, "lse": 2e-2, "grad_rel_fro": 5e-2},
+}
+
+
+def torch_dtype(w):
+    import torch
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def to_device(w, arrays, device="cuda"):
+    import torch
+    return {k: torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=torch_dtype(w))
+            for k, a in arrays.items()}
+
+
+def run_gpu(w, t, device="cuda", want_bwd=True):
+    """Runs the library on workload w with numpy inputs t; returns float64
+    numpy outputs."""
+    import torch
+    import packed_sequence_attention_amd as bd
+    seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device=device)
+    d = to_device(w, t, device)
+    o, lse = bd.attn_fwd(d["q"], d["k"], d["v"], seg, w.scale)
+    out = {"o": o, "lse": lse}
+    if want_bwd:
+        dq, dk, dv = bd.attn_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], seg, w.scale)
+        out.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {k: v.double().cpu().numpy() for k, v in out.items()}
+
+
+def oracle(w, t, rows=None, want=("fwd", "bwd"), block_rows=256):
+    from oracle import parallel
+    return parallel.run(t["q"], t["k"], t["v"], t.get("do"), w.doc_lens, w.row_offset, w.scale,
+                        block_rows=block_rows, rows=rows, want=want)
+
+
+def lse_diff(a, b):
+    """max |a - b| over finite entries; the -inf pattern must agree."""
+    fa, fb = np.isfinite(a), np.isfinite(b)
+    assert np.array_equal(fa, fb), "LSE -inf pattern differs"
+    assert np.array_equal(np.isneginf(a), np.isneginf(b))
+    return float(np.abs(a[fa] - b[fb]).max(initial=0.0))
+
+
+def rel_fro(x, ref):
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(x - ref)
+    return float(num / den) if den > 0 else float(num)
+
+
+def check(w, gpu, ref, rows=None, keys=None, report=None):
+    """Assert the tolerances; ``rows`` / ``keys`` restrict the comparison
+    (local query rows / key positions) for sampled checks.  Returns the
+    observed errors."""
+    tol = TOL[w.dtype]
+    sel_r = slice(None) if rows is None else np.asarray(rows)
+    sel_k = slice(None) if keys is None else np.asarray(keys)
+    errs = {}
+    if "o" in ref:
+        errs["o"] = float(np.abs(gpu["o"][:, sel_r] - ref["o"][:, sel_r]).max(initial=0.0))
+        errs["lse"] = lse_diff(gpu["lse"][:, :, sel_r], ref["lse"][:, :, sel_r])
+    if "dq" in ref:
+        pairs = (("dq", gpu["dq"][:, sel_r], ref["dq"][:, sel_r]), ("dk", gpu["dk"][:, sel_k], ref["dk"][:, sel_k]),
+                 ("dv", gpu["dv"][:, sel_k], ref["dv"][:, sel_k]))
+        for name, x, r in pairs:
+            if w.dtype == "f32":
+                errs[name] = float(np.abs(x - r).max(initial=0.0))
+            else:
+                errs[name] = rel_fro(x, r)
+    if report is not None:
+        report.update(errs)
+    if "o" in errs:
+        assert errs["o"] <= tol["o"], f"O max-abs {errs['o']:.3g} > {tol['o']}"
+        assert errs["lse"] <= tol["lse"], f"LSE max-abs {errs['lse']:.3g} > {tol['lse']}"
+    for name in ("dq", "dk", "dv"):
+        if name in errs:
+            lim = tol["grad_abs"] if w.dtype == "f32" else tol["grad_rel_fro"]
+            assert errs[name] <= lim, f"{name} error {errs[name]:.3g} > {lim}"
+    return errs
+
+
+def small_case(i, dtype, doc_lens, seq_len, row_offset, q_len, h_q, h_kv, d, scale=None):
+    w = synthetic.custom_workload(1000 + i, dtype, doc_lens, seq_len, row_offset, q_len, h_q, h_kv, d,
+                                  scale, name=f"case{i}")
+    return w, synthetic.draw_tensors(w)

@@ -1,0 +1,122 @@
+"""GPU invariants of the HIP path that hold at any size:
+
+* chunk concatenation (key property 1 of the Automodel page "feat(
+  distributed): block-diagonal varlen CP for packed sequences"): O and LSE of
+  contiguous chunks concatenated equal the single full call bit for bit
+  (key tiles are anchored at fixed positions of the row, so a row's
+  arithmetic does not depend on the chunk); dQ concatenates and dK/dV sum
+  over chunks to the full call's within tolerance;
+* the forward is bitwise deterministic (a replayed forward under activation
+  checkpointing equals the original, Design overview, packed.py) and so are
+  dK and dV;
+* documents are independent: changing one document's inputs leaves every
+  other document's O, LSE, dK and dV bit for bit unchanged;
+* the autograd wrapper returns the raw calls' results.
+"""
+import numpy as np
+import pytest
+
+import synthetic
+from tests import helpers as H
+
+gpu = pytest.mark.gpu
+
+
+def _w2_small():
+    # workload-2-like packing at S = 2048 (lognormal doc lengths), bf16 32/8/128
+    rng = np.random.default_rng(7)
+    lens, tot = [], 0
+    while tot < 2048:
+        Ln = int(min(max(int(np.rint(rng.lognormal(np.log(300), 1.0))), 16), 2048 - tot)); lens.append(Ln); tot += Ln
+    return lens
+
+
+@gpu
+@pytest.mark.parametrize("cp", [2, 4, 8])
+def test_chunk_concatenation(cp):
+    import torch
+    import packed_sequence_attention_amd as bd
+    docs = [_w2_small()]
+    S = 2048
+    w, t = H.small_case(200 + cp, "bf16", docs, S, 0, S, 32, 8, 128)
+    d = H.to_device(w, t)
+    full = bd.segment(docs, S, 0, S, device="cuda")
+    o, lse = bd.attn_fwd(d["q"], d["k"], d["v"], full)
+    dq, dk, dv = bd.attn_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], full)
+    dk_sum = torch.zeros_like(dk, dtype=torch.float32)
+    dv_sum = torch.zeros_like(dv, dtype=torch.float32)
+    bounds = np.linspace(0, S, cp + 1).astype(int)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        seg = bd.segment(docs, S, int(a), int(b - a), device="cuda")
+        qc = d["q"][:, a:b].contiguous(); doc_ = d["do"][:, a:b].contiguous()
+        oc, lc = bd.attn_fwd(qc, d["k"], d["v"], seg)
+        assert torch.equal(oc, o[:, a:b]), "O differs from the full call"
+        assert torch.equal(lc, lse[:, :, a:b]), "LSE differs from the full call"
+        dqc, dkc, dvc = bd.attn_bwd(qc, d["k"], d["v"], oc, lc, doc_, seg)
+        assert H.rel_fro(dqc.double().cpu().numpy(), dq[:, a:b].double().cpu().numpy()) < 1e-2
+        dk_sum += dkc.float(); dv_sum += dvc.float()
+    assert H.rel_fro(dk_sum.double().cpu().numpy(), dk.double().cpu().numpy()) < 1e-2
+    assert H.rel_fro(dv_sum.double().cpu().numpy(), dv.double().cpu().numpy()) < 1e-2
+
+
+@gpu
+def test_determinism():
+    import torch
+    import packed_sequence_attention_amd as bd
+    w = synthetic.workload(2)
+    t = synthetic.draw_tensors(w)
+    d = H.to_device(w, t)
+    seg = bd.segment(w.doc_lens, w.seq_len, 0, w.q_len, device="cuda")
+    o1, l1 = bd.attn_fwd(d["q"], d["k"], d["v"], seg)
+    o2, l2 = bd.attn_fwd(d["q"], d["k"], d["v"], seg)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = bd.attn_bwd(d["q"], d["k"], d["v"], o1, l1, d["do"], seg)
+    g2 = bd.attn_bwd(d["q"], d["k"], d["v"], o1, l1, d["do"], seg)
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    assert H.rel_fro(g1[0].double().cpu().numpy(), g2[0].double().cpu().numpy()) < 1e-3
+
+
+@gpu
+def test_document_independence():
+    import torch
+    import packed_sequence_attention_amd as bd
+    docs = [[300, 257, 500, 91, 400]]
+    S = 1548
+    w, t = H.small_case(300, "bf16", docs, S, 0, S, 8, 2, 128)
+    lo, hi = 300, 557
+    t2 = {k: v.copy() for k, v in t.items()}
+    rng = np.random.default_rng(1)
+    for k in t2:
+        t2[k][:, lo:hi] = synthetic.round_bf16(t2[k][:, lo:hi] + rng.standard_normal(t2[k][:, lo:hi].shape,
+                                                                                     dtype=np.float32))
+    seg = bd.segment(docs, S, 0, S, device="cuda")
+    outs = []
+    for tt in (t, t2):
+        d = H.to_device(w, tt)
+        o, lse = bd.attn_fwd(d["q"], d["k"], d["v"], seg)
+        dq, dk, dv = bd.attn_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], seg)
+        outs.append((o, lse, dk, dv))
+    keep = torch.ones(S, dtype=torch.bool); keep[lo:hi] = False
+    (o1, l1, k1, v1), (o2, l2, k2, v2) = outs
+    assert torch.equal(o1[:, keep], o2[:, keep])
+    assert torch.equal(l1[:, :, keep], l2[:, :, keep])
+    assert torch.equal(k1[:, keep], k2[:, keep]) and torch.equal(v1[:, keep], v2[:, keep])
+    assert not torch.equal(o1[:, lo:hi], o2[:, lo:hi])
+
+
+@gpu
+def test_autograd_wrapper_matches_raw_calls():
+    import torch
+    import packed_sequence_attention_amd as bd
+    docs = [[100, 156]]
+    w, t = H.small_case(400, "bf16", docs, 256, 0, 256, 8, 2, 64)
+    d = H.to_device(w, t)
+    seg = bd.segment(docs, 256, 0, 256, device="cuda")
+    q = d["q"].clone().requires_grad_(); k = d["k"].clone().requires_grad_(); v = d["v"].clone().requires_grad_()
+    out = bd.attention(q, k, v, seg)
+    out.backward(d["do"])
+    o, lse = bd.attn_fwd(d["q"], d["k"], d["v"], seg)
+    dq, dk, dv = bd.attn_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], seg)
+    assert torch.equal(out.detach(), o)
+    assert torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
+    assert H.rel_fro(q.grad.double().cpu().numpy(), dq.double().cpu().numpy()) < 1e-3
