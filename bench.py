@@ -1,0 +1,250 @@
+"""Benchmark of the block-diagonal packed attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+host segmentation of the document lengths (blockdiag_segment), the pinned
+upload and device metadata build (blockdiag_meta_build), the forward
+(blockdiag_attn_fwd) and the backward (blockdiag_attn_bwd).  Inputs are
+resident in HBM before the timed region starts.
+
+Metric: useful (unmasked-pair) attention TFLOP/s, counting 4*d*H_q FLOP per
+allowed (query, key) pair for the forward and 2.5 times that for the
+backward; `value` divides that by the whole step's wall time.  The default
+workload is bf16 B=2, S=4096 per row, H_q=32, H_kv=8, d=128, lognormal
+document lengths (median 512), row_offset 0.
+
+Printed: one JSON line (rank 0), with
+  roofline      the backward's main kernel (the dominant one): algorithmic
+                FLOP per launch / its mean duration from HIP events recorded
+                around that kernel on its stream, against the bf16 dense
+                matrix-core peak; `traffic` from the committed rocprofv3
+                counter summary when it was taken on the current kernel
+                source, else null;
+  cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
+                sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "unmasked-pair attention TFLOP/s fwd+bwd (bf16, packed S=4k) and % MFMA peak"
+
+
+def useful_pairs(seg):
+    """Allowed (query, key) pairs per query head, from the segment table:
+    segment rows t = 0..q-1 see t + (k - q) + 1 keys (bottom-right aligned),
+    padding segments (k = 0) none."""
+    total = 0
+    for s in range(seg.n_seg):
+        qn = int(seg.cu_q[s + 1] - seg.cu_q[s])
+        kn = int(seg.cu_k[s + 1] - seg.cu_k[s])
+        if kn > 0:
+            total += qn * (kn - qn + 1) + qn * (qn - 1) // 2
+    return total
+
+
+class HipEvents:
+    """Minimal hipEvent_t handling through the HIP runtime's C API."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def kernel_source_digest(name):
+    path = os.path.join(ROOT, "packed_sequence_attention_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file, workload_tag):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_traffic.md when
+    its recorded source digest matches the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_file.split('.')[0]}_{workload_tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_d = re.search(r"source_digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_d or not m_b or m_d.group(1) != kernel_source_digest(kernel_file):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, t, flops_per_pair, budget_units=None):
+    """The fp64 oracle (windowed, unchanged) on a bounded sample: the first
+    `budget_units` (batch row, K/V head) sub-problems of the workload, each a
+    K/V head's query-head group over the whole row, forward and backward, in
+    a pool of worker processes with one BLAS thread each."""
+    import numpy as np
+    from oracle import parallel
+    B, Hkv = w.batch, w.h_kv
+    units = [(b, g) for b in range(B) for g in range(Hkv)]
+    n_units = budget_units or len(units)
+    G = w.h_q // w.h_kv
+    # the sample: batch row 0, K/V heads 0..n-1 (contiguous slices of the same tensors)
+    n_heads = min(n_units, Hkv)
+    sub_q = np.ascontiguousarray(t["q"][:1, :, :n_heads * G])
+    sub_do = np.ascontiguousarray(t["do"][:1, :, :n_heads * G])
+    sub_k = np.ascontiguousarray(t["k"][:1, :, :n_heads])
+    sub_v = np.ascontiguousarray(t["v"][:1, :, :n_heads])
+    workers = parallel.default_workers()
+    t0 = time.perf_counter()
+    parallel.run(sub_q, sub_k, sub_v, sub_do, w.doc_lens[:1], w.row_offset, w.scale, block_rows=256,
+                 workers=workers)
+    dt = time.perf_counter() - t0
+    from oracle import attention as A
+    pairs = A.useful_pairs(w.doc_lens[:1], w.seq_len, w.row_offset, w.q_len)
+    flops = flops_per_pair * n_heads * G * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(workers, n_heads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"batch row 0, K/V heads 0..{n_heads - 1} ({n_heads * G} query heads) of the "
+                      f"workload, forward+backward, fp64 numpy windowed oracle"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default 2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU's share only: run it with --gpus 1 (the multi-GPU exchange "
+              "around the kernel is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import packed_sequence_attention_amd as bd
+    import synthetic
+
+    if not os.path.exists(bd.library_path()):
+        from packed_sequence_attention_amd import build
+        build.build_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synthetic.workload(args.workload)
+    t = synthetic.draw_tensors(w)
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    d = {k: torch.from_numpy(v).to(dev, dt) for k, v in t.items()}
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    seg0 = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len)
+    pairs = useful_pairs(seg0)
+    D, Hq = w.head_dim, w.h_q
+    flops_fwd = 4 * D * Hq * pairs
+    flops_bwd = 10 * D * Hq * pairs
+    ev = HipEvents()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(marks=None):
+        seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device=dev)
+        if marks is not None:
+            bd.mark_main_kernel(marks[0], marks[1])
+        o, lse = bd.attn_fwd(q, k, v, seg, w.scale)
+        if marks is not None:
+            bd.mark_main_kernel(marks[2], marks[3])
+        dq, dk, dv = bd.attn_bwd(q, k, v, o, lse, do, seg, w.scale)
+        return o, dq
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    marks = [[ev.create() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(marks[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = [ev.elapsed_ms(m[0], m[1]) for m in marks]
+    bwd_ms = [ev.elapsed_ms(m[2], m[3]) for m in marks]
+    for m in marks:
+        for e in m:
+            ev.destroy(e)
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+
+    # kernel-only fwd+bwd entry-point times (events around each call), for the
+    # fwd+bwd figure that excludes once-per-step metadata work
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device=dev)
+    times_f, times_b = [], []
+    for _ in range(max(5, args.steps // 2)):
+        e[0].record(stream)
+        o, lse = bd.attn_fwd(q, k, v, seg, w.scale)
+        e[1].record(stream)
+        bd.attn_bwd(q, k, v, o, lse, do, seg, w.scale)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        times_f.append(e[0].elapsed_time(e[1]))
+        times_b.append(e[1].elapsed_time(e[2]))
+    tf = float(np.median(times_f))
+    tb = float(np.median(times_b))
+
+    value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
+    achieved = flops_bwd / (bwd_avg * 1e-3) / 1e12
+    traffic = traffic_from_profile("bwd_mfma.hip", f"w{args.workload}") if w.dtype == "bf16" else None
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "row_offset": w.row_offset,
+                   "q_len": w.q_len, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim,
+                   "n_docs": w.n_docs, "useful_pairs_per_head": pairs, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_bwd_entry_ms": {"fwd": round(tf, 4), "bwd": round(tb, 4)},
+        "tflops_fwd_plus_bwd_calls": round((flops_fwd + flops_bwd) / ((tf + tb) * 1e-3) / 1e12, 3),
+        "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd": round(bwd_avg, 4)},
+        "fwd_kernel_tflops": round(flops_fwd / (fwd_avg * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "mfma", "kernel": "bwd_mfma_kernel", "achieved": round(achieved, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, t, 14 * D)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -200,6 +200,19 @@ bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
                              const int32_t *d_meta, void *dq, void *dk, void *dv,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * blockdiag_mark_main_kernel -- profiling hook.  The next blockdiag_attn_fwd
+ * or blockdiag_attn_bwd call made on this thread records start_event on its
+ * stream right before launching its main attention kernel and stop_event
+ * right after it (the backward's row-statistics and dQ-conversion kernels
+ * fall outside the pair), then forgets both.  The events are hipEvent_t
+ * handles passed as void*, created and owned by the caller; NULL, NULL
+ * clears a pending request.  Lets a caller time the dominant kernel with
+ * events on the stream it runs on.  Returns BD_OK, or BD_ERR_INVALID_ARG
+ * if exactly one handle is NULL.
+ */
+bd_status blockdiag_mark_main_kernel(void *start_event, void *stop_event);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char *blockdiag_last_error(void);
 

@@ -46,7 +46,7 @@ STATUS = {0: "BD_OK", 1: "BD_ERR_INVALID_ARG", 2: "BD_ERR_BAD_METADATA", 3: "BD_
           4: "BD_ERR_WORKSPACE", 5: "BD_ERR_UNSUPPORTED", 6: "BD_ERR_HIP"}
 EXPORTS = ("blockdiag_segment", "blockdiag_validate", "blockdiag_meta_ints", "blockdiag_meta_build",
            "blockdiag_workspace_bytes", "blockdiag_attn_fwd", "blockdiag_attn_bwd",
-           "blockdiag_last_error", "blockdiag_version")
+           "blockdiag_mark_main_kernel", "blockdiag_last_error", "blockdiag_version")
 
 
 class BlockdiagError(RuntimeError):
@@ -87,6 +87,8 @@ def load_library():
     lib.blockdiag_attn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                        p, p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.blockdiag_attn_bwd.restype = ctypes.c_int
+    lib.blockdiag_mark_main_kernel.argtypes = [p, p]
+    lib.blockdiag_mark_main_kernel.restype = ctypes.c_int
     lib.blockdiag_last_error.argtypes = []
     lib.blockdiag_last_error.restype = ctypes.c_char_p
     lib.blockdiag_version.argtypes = []
@@ -125,19 +127,21 @@ class SegTable:
     max_k: int
     table: object = None
     meta: object = None
+    _pinned: object = None
 
     def to(self, device):
         """Upload the table and build the device metadata on ``device``."""
         import torch
         lib = load_library()
-        host = np.concatenate([self.cu_q, self.cu_k, self.k_begin]).astype(np.int32)
-        table = torch.from_numpy(host).to(device)
+        host = torch.from_numpy(np.concatenate([self.cu_q, self.cu_k, self.k_begin]).astype(np.int32))
+        pinned = host.pin_memory()
+        table = pinned.to(device, non_blocking=True)  # no host sync; pinned copy kept alive below
         n_meta = lib.blockdiag_meta_ints(self.batch, self.seq_len, self.q_len)
         meta = torch.empty(max(int(n_meta), 1), dtype=torch.int32, device=device)
         stream = torch.cuda.current_stream(device).cuda_stream
         _check(lib.blockdiag_meta_build(table.data_ptr(), self.n_seg, self.batch, self.seq_len,
                                         self.row_offset, self.q_len, meta.data_ptr(), stream))
-        return dataclasses.replace(self, table=table, meta=meta)
+        return dataclasses.replace(self, table=table, meta=meta, _pinned=pinned)
 
     def meta_views(self):
         """(row_lo, row_hi, key_qlo, key_qhi) views of the device metadata."""
@@ -245,6 +249,13 @@ def _shapes(q, k, v, seg):
     if seg.meta is None or seg.meta.device != q.device:
         raise BlockdiagError(1, "segment table has no device metadata on the tensors' device")
     return B, L, Hq, d, S, Hkv
+
+
+def mark_main_kernel(start_event, stop_event):
+    """Profiling hook (``blockdiag_mark_main_kernel``): the next attn_fwd /
+    attn_bwd call records these hipEvent_t handles (ints) around its main
+    kernel on its stream."""
+    _check(load_library().blockdiag_mark_main_kernel(start_event, stop_event))
 
 
 def attn_fwd(q, k, v, seg, scale=None):

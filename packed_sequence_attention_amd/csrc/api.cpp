@@ -42,7 +42,26 @@ bool use_mfma(bd_dtype dtype, int32_t head_dim, int32_t h_q, int32_t h_kv, float
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+thread_local hipEvent_t g_mark_start = nullptr;
+thread_local hipEvent_t g_mark_stop = nullptr;
+
+// Takes the pending profiling marks (they apply to one call only).
+void take_marks(hipEvent_t* start, hipEvent_t* stop) {
+  *start = g_mark_start;
+  *stop = g_mark_stop;
+  g_mark_start = g_mark_stop = nullptr;
+}
+
 }  // namespace
+
+extern "C" bd_status blockdiag_mark_main_kernel(void* start_event, void* stop_event) {
+  bd::clear_error();
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(BD_ERR_INVALID_ARG, "both events or neither");
+  g_mark_start = static_cast<hipEvent_t>(start_event);
+  g_mark_stop = static_cast<hipEvent_t>(stop_event);
+  return BD_OK;
+}
 
 extern "C" size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_len) {
   if (batch < 0 || seq_len < 0 || q_len < 0) return 0;
@@ -92,7 +111,8 @@ extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t s
   const size_t need = blockdiag_workspace_bytes(0, dtype, batch, seq_len, q_len, h_q, h_kv, head_dim);
   if (workspace_bytes < need) return fail(BD_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   bd::FwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
-                q, k, v, d_meta, o, lse};
+                q, k, v, d_meta, o, lse, nullptr, nullptr};
+  take_marks(&a.mark_start, &a.mark_stop);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma(dtype, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
                                                              : bd::launch_fwd_generic(a, s);
@@ -130,7 +150,8 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
   bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
                 q, k, v, o, lse, d_o, d_meta, dq, dk, dv,
                 reinterpret_cast<float*>(ws),
-                mf ? reinterpret_cast<float*>(ws + align256(rows * sizeof(float))) : nullptr};
+                mf ? reinterpret_cast<float*>(ws + align256(rows * sizeof(float))) : nullptr, nullptr, nullptr};
+  take_marks(&a.mark_start, &a.mark_stop);
   hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return BD_OK;

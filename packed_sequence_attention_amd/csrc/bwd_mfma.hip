@@ -334,11 +334,15 @@ hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
   const int n_kt = (a.seq_len + kKB - 1) / kKB;
   const int64_t grid = static_cast<int64_t>(n_kt) * a.batch * a.h_kv;
   if (grid > 0) {
+    e = mark(a.mark_start, st);
+    if (e != hipSuccess) return e;
     bwd_mfma_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
         s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.lse, a.delta, m,
         a.dq_acc, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = mark(a.mark_stop, st);
     if (e != hipSuccess) return e;
   }
   const int64_t n8 = static_cast<int64_t>(a.batch) * a.q_len * a.h_q * D / 8;

@@ -229,10 +229,14 @@ hipError_t fwd_mfma_t(const FwdArgs& a, hipStream_t st) {
   const int n_qt = (a.q_len + kBM - 1) / kBM;
   const int n_hg = a.h_q / 4;
   const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
+  hipError_t e = mark(a.mark_start, st);
+  if (e != hipSuccess) return e;
   fwd_mfma_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), m, static_cast<uint16_t*>(a.o), a.lse, n_qt, n_hg);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return mark(a.mark_stop, st);
 }
 
 }  // namespace

@@ -309,10 +309,14 @@ hipError_t fwd_generic_t(const FwdArgs& a, hipStream_t st) {
   AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int64_t waves = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
+  hipError_t e = mark(a.mark_start, st);
+  if (e != hipSuccess) return e;
   fwd_generic_kernel<T, NR><<<blocks_for(waves), 256, 0, st>>>(
       s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v), m,
       static_cast<T*>(a.o), a.lse);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return mark(a.mark_stop, st);
 }
 
 template <typename T, int NR>
@@ -330,11 +334,15 @@ hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t keys = static_cast<int64_t>(a.batch) * a.seq_len * a.h_kv;
+  e = mark(a.mark_start, st);
+  if (e != hipSuccess) return e;
   dkv_generic_kernel<T, NR><<<blocks_for(keys), 256, 0, st>>>(
       s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
       static_cast<const T*>(a.d_o), a.lse, a.delta, m, static_cast<T*>(a.dk),
       static_cast<T*>(a.dv));
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return mark(a.mark_stop, st);
 }
 
 template <typename T>

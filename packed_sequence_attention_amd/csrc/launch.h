@@ -19,6 +19,8 @@ struct FwdArgs {
   const int32_t* meta;
   void* o;
   float* lse;
+  hipEvent_t mark_start;  // recorded around the main kernel when non-null
+  hipEvent_t mark_stop;
 };
 
 struct BwdArgs {
@@ -37,6 +39,8 @@ struct BwdArgs {
   void* dv;
   float* delta;   // workspace: [batch][h_q][q_len]
   float* dq_acc;  // workspace: [batch][q_len][h_q][head_dim] (matrix-core path only)
+  hipEvent_t mark_start;  // recorded around the main kernel when non-null
+  hipEvent_t mark_stop;
 };
 
 // Metadata expansion (segment table -> per-row / per-key bounds).
@@ -58,5 +62,10 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
 
 // Fill n 16-bit words with zeros (a kernel, so it is safe under graph capture).
 hipError_t launch_zero_u16(void* p, int64_t n, hipStream_t stream);
+
+// Records a profiling mark on the stream when the event is non-null.
+inline hipError_t mark(hipEvent_t ev, hipStream_t stream) {
+  return ev != nullptr ? hipEventRecord(ev, stream) : hipSuccess;
+}
 
 }  // namespace bd
