@@ -40,6 +40,10 @@ bool use_mfma(bd_dtype dtype, int32_t head_dim, int32_t h_q, int32_t h_kv, float
   return bd::mfma_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f;
 }
 
+bool use_mfma_bwd(bd_dtype dtype, int32_t q_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
+  return use_mfma(dtype, head_dim, h_q, h_kv, scale) && bd::bwd_mfma_fits(q_len, h_q, head_dim);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 thread_local hipEvent_t g_mark_start = nullptr;
@@ -93,7 +97,7 @@ extern "C" size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t 
   if (!is_bwd || batch <= 0 || q_len <= 0 || h_q <= 0 || head_dim <= 0) return 0;
   const size_t rows = static_cast<size_t>(batch) * q_len * h_q;
   size_t bytes = align256(rows * sizeof(float));  // delta
-  if (use_mfma(dtype, head_dim, h_q, h_kv, 1.f)) bytes += align256(rows * head_dim * sizeof(float));
+  if (use_mfma_bwd(dtype, q_len, head_dim, h_q, h_kv, 1.f)) bytes += align256(rows * head_dim * sizeof(float));
   return bytes;
 }
 
@@ -146,7 +150,7 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
   }
   const size_t rows = static_cast<size_t>(batch) * q_len * h_q;
   char* ws = static_cast<char*>(workspace);
-  const bool mf = use_mfma(dtype, head_dim, h_q, h_kv, scale);
+  const bool mf = use_mfma_bwd(dtype, q_len, head_dim, h_q, h_kv, scale);
   bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
                 q, k, v, o, lse, d_o, d_meta, dq, dk, dv,
                 reinterpret_cast<float*>(ws),

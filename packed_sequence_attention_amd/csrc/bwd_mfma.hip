@@ -19,11 +19,23 @@
 //                                    load, B = P / dS from the accumulators)
 // dS^T is written to LDS; then the tile's dQ (32 rows x head_dim) is computed
 // over all 128 keys (A = dS via transpose load, B = K via transpose load) and
-// added to a float32 accumulator with float32 atomics; a final kernel scales
-// and rounds it.  dK and dV stay in registers until the end and are written
-// once (deterministic).  Elements outside the block-causal mask are zeroed
-// only on tiles that are not entirely allowed; waves whose keys no row of
-// the tile attends skip the tile.
+// added to a float32 accumulator with buffer atomics (the buffer's range
+// check drops rows past the chunk); a final kernel scales and rounds it.
+// dK and dV stay in registers until the end and are written once
+// (deterministic).  The element mask uses the per-key row interval
+// [key_qlo, key_qhi) and is applied only to blocks that are not entirely
+// allowed; waves whose keys no row of the tile attends skip the tile.
+//
+// LDS layouts are chosen so every access pattern is free of bank conflicts
+// (64 banks of 4 bytes; 16-byte reads serve 16 lanes per cycle, 8-byte reads
+// and transpose loads 32 lanes):
+//   Q / dO tiles: rows of head_dim bf16 without padding; the 16-byte chunk c
+//   of row r is stored at chunk c ^ f(r), with f chosen so that 16 rows of a
+//   row read and 4 rows x 4 chunks of a transpose read all land on distinct
+//   banks.  K tile: rows padded by 64 bytes.  dS^T: 64-byte rows with the
+//   chunk index xor-ed by bits 2..3 of the row.
+// Q / dO / LSE / delta of the next query tile are loaded into registers
+// while the current one is processed (LDS double buffer).
 #include <limits.h>
 #include <math.h>
 
@@ -38,19 +50,28 @@ constexpr int kQB = 32;   // query rows per tile
 
 template <int D>
 struct BwdLds {
-  static constexpr int KP = D * 2 + 64;  // K tile, read by transpose loads
-  static constexpr int QP = D * 2 + 32;  // Q / dO tiles, read both ways
-  static constexpr int SP = kQB * 2;     // dS^T rows (keys) of 32 bf16
-  static constexpr int off_q = kKB * KP;
-  static constexpr int off_do = off_q + kQB * QP;
-  static constexpr int off_ds = off_do + kQB * QP;
-  static constexpr int off_stat = off_ds + kKB * SP;
-  static constexpr int bytes = off_stat + 4 * kQB * 4 + 16 * 4;
+  static constexpr int KP = D * 2 + 64;  // K tile row pitch (transpose loads)
+  static constexpr int QP = D * 2;       // Q / dO tile row pitch (xor-swizzled chunks)
+  static constexpr int SP = kQB * 2;     // dS^T row pitch (32 bf16)
+  static constexpr int stat = 2 * kQB * 4;          // lse * log2(e), delta
+  static constexpr int qbuf = 2 * kQB * QP + stat;  // one Q/dO/statistics buffer
+  static constexpr int off_q = kKB * KP;            // two qbuf follow the K tile
+  static constexpr int off_ds = off_q + 2 * qbuf;
+  static constexpr int off_red = off_ds + kKB * SP;
+  static constexpr int bytes = off_red + 16 * 4;
+  static constexpr int NCH = kQB * (D / 8) / 256;   // 16-byte chunks per thread per tensor
 };
 
-__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, int second_off) {
+// Chunk swizzle of row r of a Q / dO tile (see the file comment).
+template <int D>
+__device__ __forceinline__ int qswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + second_off));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
   const auto ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
@@ -65,16 +86,11 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
   using L = BwdLds<D>;
+  constexpr int NCH = L::NCH;
   __shared__ __attribute__((aligned(16))) char smem[L::bytes];
   char* sK = smem;
-  char* sQ = smem + L::off_q;
-  char* sdO = smem + L::off_do;
   char* sdS = smem + L::off_ds;
-  float* sLse = reinterpret_cast<float*>(smem + L::off_stat);
-  float* sDel = sLse + kQB;
-  int* sLo = reinterpret_cast<int*>(sDel + kQB);
-  int* sHi = sLo + kQB;
-  int* sRed = sHi + kQB;  // 16 ints of reduction scratch
+  int* sRed = reinterpret_cast<int*>(smem + L::off_red);  // 16 ints of reduction scratch
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
@@ -110,8 +126,8 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
           k + ((static_cast<int64_t>(b) * s.seq_len + j) * s.h_kv + g) * D + col * 8);
     *reinterpret_cast<uint4*>(sK + r * L::KP + col * 16) = x;
   }
-  // Query rows attending this wave's keys and the workgroup's keys.
-  int qlo_k = INT_MAX, qhi_k = 0;
+  // Local rows attending this lane's key: [qlo_k, qhi_k) (empty: qlo_k >= qhi_k).
+  int qlo_k = INT_MAX, qhi_k = INT_MIN;
   if (key_ok) {
     const int64_t kidx = static_cast<int64_t>(b) * s.seq_len + key;
     const int a0 = m.key_qlo[kidx], a1 = m.key_qhi[kidx];
@@ -121,6 +137,11 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
     }
   }
   const int wqlo = wave_min_i(qlo_k), wqhi = wave_max_i(qhi_k);
+  // Rows every key of the wave attends: [wfull_lo, wfull_hi).
+  const int wfull_lo = wave_max_i(qlo_k), wfull_hi = wave_min_i(qhi_k);
+  // Element mask: row t is allowed iff (unsigned)(t - mask_lo) < mask_span.
+  const int mask_lo = qhi_k > qlo_k ? qlo_k : 0;
+  const unsigned mask_span = qhi_k > qlo_k ? static_cast<unsigned>(qhi_k - qlo_k) : 0u;
   if (lane == 0) {
     sRed[wave] = wqlo;
     sRed[4 + wave] = wqhi;
@@ -136,157 +157,216 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
     for (int j = 0; j < 16; ++j) dkacc[db][j] = dvacc[db][j] = 0.f;
 
   const float c = s.scale * kLog2e;
-  // Per-lane LDS offsets.
-  const int nat_rd = n * L::QP + kg * 16;                       // natural 16-byte row reads
-  const int tr_row = 4 * kg + ((lane & 15) >> 2);               // transpose-load row within 8
-  const int tr_col = (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;  // byte column
+  // Per-lane LDS addressing.
+  const int tr_row = 4 * kg + ((lane & 15) >> 2);   // transpose-load row within a group of 8
+  const int tr_g = (lane >> 4) & 1;                 // 16-column half of a transpose load
+  const int tr_s = lane & 3;                        // 4-column quarter
+  const int tr_col = (16 * tr_g + 4 * tr_s) * 2;    // byte column (unswizzled layouts)
   // dQ split: wave -> (d block, key part).
-  constexpr int DQ_PARTS = 4 / DB;            // key parts per d block
-  constexpr int DQ_KEYS = kKB / DQ_PARTS;     // keys per wave in the dQ product
+  constexpr int DQ_PARTS = 4 / DB;
+  constexpr int DQ_KEYS = kKB / DQ_PARTS;
   const int dq_db = wave % DB;
   const int dq_k0 = (wave / DB) * DQ_KEYS;
+  // dQ accumulator rows of (b, h) are addressed through a buffer whose range
+  // ends at row q_len, so rows past the chunk are dropped by the hardware.
+  const int row_stride = s.h_q * D;  // elements between consecutive rows
+  const int dq_voff = ((kg * 4) * row_stride + dq_db * 32 + n) * 4;
 
-  if (gqhi > gqlo) {
-    const int qt0 = gqlo / kQB, qt1 = (gqhi - 1) / kQB;
-    for (int hh = 0; hh < s.group; ++hh) {
-      const int h = g * s.group + hh;
-      for (int qt = qt0; qt <= qt1; ++qt) {
-        const int t0 = qt * kQB;
-        __syncthreads();
-        // Stage Q, dO rows and their statistics.
-        for (int ci = tid; ci < kQB * CH; ci += 256) {
-          const int r = ci / CH, col = ci % CH;
-          const int t = t0 + r;
-          uint4 xq = make_uint4(0, 0, 0, 0), xo = make_uint4(0, 0, 0, 0);
-          if (t < s.q_len) {
-            const int64_t off = ((static_cast<int64_t>(b) * s.q_len + t) * s.h_q + h) * D + col * 8;
-            xq = *reinterpret_cast<const uint4*>(q + off);
-            xo = *reinterpret_cast<const uint4*>(d_o + off);
+  // Q / dO / statistics staging: global -> registers (one iteration ahead)
+  // -> LDS double buffer.  Iteration it covers query head g*group + it / n_q
+  // and the query tile qt0 + it % n_q.
+  uint4 qx[NCH], ox[NCH];
+  float st_lse = 0.f, st_del = 0.f;
+  const int qt0 = gqlo / kQB;
+  const int n_q = gqhi > gqlo ? (gqhi - 1) / kQB - qt0 + 1 : 0;
+  const int n_it = n_q * s.group;
+  auto load_it = [&](int it) {
+    const int h = g * s.group + it / n_q;
+    const int t0 = (qt0 + it % n_q) * kQB;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = tid + 256 * i;
+      const int r = ci / CH, col = ci % CH;
+      const int t = t0 + r;
+      qx[i] = make_uint4(0, 0, 0, 0);
+      ox[i] = make_uint4(0, 0, 0, 0);
+      if (t < s.q_len) {
+        const int64_t off = ((static_cast<int64_t>(b) * s.q_len + t) * s.h_q + h) * D + col * 8;
+        qx[i] = *reinterpret_cast<const uint4*>(q + off);
+        ox[i] = *reinterpret_cast<const uint4*>(d_o + off);
+      }
+    }
+    if (tid < kQB) {
+      const int t = t0 + tid;
+      st_lse = 0.f;
+      st_del = 0.f;
+      if (t < s.q_len) {  // padding rows (LSE = -inf) are masked out later
+        const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
+        st_lse = lse[st];
+        st_del = delta[st];
+      }
+    }
+  };
+  auto store_it = [&](int buf) {
+    char* sQ = smem + L::off_q + buf * L::qbuf;
+    char* sdO = sQ + kQB * L::QP;
+    float* stat = reinterpret_cast<float*>(sdO + kQB * L::QP);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = tid + 256 * i;
+      const int r = ci / CH, col = ci % CH;
+      const int pos = r * L::QP + ((col ^ qswz<D>(r)) << 4);
+      *reinterpret_cast<uint4*>(sQ + pos) = qx[i];
+      *reinterpret_cast<uint4*>(sdO + pos) = ox[i];
+    }
+    if (tid < kQB) {
+      stat[tid] = st_lse * kLog2e;
+      stat[kQB + tid] = st_del;
+    }
+  };
+
+  if (n_it > 0) {
+    load_it(0);
+    store_it(0);
+    __syncthreads();
+  }
+  for (int it = 0; it < n_it; ++it) {
+    const int buf = it & 1;
+    const bool more = it + 1 < n_it;
+    if (more) load_it(it + 1);  // in flight during this iteration's math
+    const int h = g * s.group + it / n_q;
+    const int t0 = (qt0 + it % n_q) * kQB;
+    const char* sQ = smem + L::off_q + buf * L::qbuf;
+    const char* sdO = sQ + kQB * L::QP;
+    const float* sLse = reinterpret_cast<const float*>(sdO + kQB * L::QP);
+    const float* sDel = sLse + kQB;
+    const bool active = wqlo < t0 + kQB && wqhi > t0;
+    const int krow = wave * 32 + n;
+    char* dsrow = sdS + krow * L::SP + kg * 8;
+    const int ksw = (krow >> 2) & 3;
+    // P and dS as bf16 B operands (k = query rows in accumulator order);
+    // zero on waves whose keys no row of this tile attends, so the dV / dK
+    // products below run unconditionally and their accumulators stay put.
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[0][i] = pb[1][i] = dsb[0][i] = dsb[1][i] = static_cast<__bf16>(0.f);
+    if (active) {
+      f32x16 sacc, pacc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
+      const int nat_row = n * L::QP;
+      const int nat_swz = qswz<D>(n);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int pos = nat_row + (((2 * kk + kg) ^ nat_swz) << 4);
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + pos);
+        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sdO + pos);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], pacc, 0, 0, 0);
+      }
+      // sacc[j] = S[row (j/4)*8 + kg*4 + j%4][key n]
+      float dsv[16];
+      float pv[16];
+      // every (row, key) pair of this 32x32 block allowed?  (uniform branch)
+      if (wfull_lo <= t0 && t0 + kQB <= wfull_hi) {
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const int r0 = jq * 8 + kg * 4;
+          const float4 ls4 = *reinterpret_cast<const float4*>(sLse + r0);
+          const float4 de4 = *reinterpret_cast<const float4*>(sDel + r0);
+          const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
+          const float dev[4] = {de4.x, de4.y, de4.z, de4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = jq * 4 + e;
+            pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
+            dsv[j] = pv[j] * (pacc[j] - dev[e]);
           }
-          *reinterpret_cast<uint4*>(sQ + r * L::QP + col * 16) = xq;
-          *reinterpret_cast<uint4*>(sdO + r * L::QP + col * 16) = xo;
         }
-        if (tid < kQB) {
-          const int t = t0 + tid;
-          float ls = 0.f, de = 0.f;
-          int lo = 0, hi = 0;
-          if (t < s.q_len) {
-            const int64_t bt = static_cast<int64_t>(b) * s.q_len + t;
-            lo = m.row_lo[bt];
-            hi = m.row_hi[bt];
-            const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
-            if (hi > lo) {
-              ls = lse[st] * kLog2e;
-              de = delta[st];
-            }
-          }
-          sLse[tid] = ls;
-          sDel[tid] = de;
-          sLo[tid] = lo;
-          sHi[tid] = hi;
-        }
-        __syncthreads();
-        const bool active = wqlo < t0 + kQB && wqhi > t0;
-        char* dsrow = sdS + (wave * 32 + n) * L::SP + kg * 8;
-        if (active) {
-          // Is every (row, key) pair of this 32x32 block allowed?
-          const int rlo = sLo[n], rhi = sHi[n];
-          const bool rreal = rhi > rlo;
-          const bool full = wave_min_i(rreal ? 1 : 0) == 1 && wave_max_i(rlo) <= kw0 &&
-                            kw0 + 31 <= s.row_offset + t0;
-          f32x16 sacc, pacc;
+      } else {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
+        for (int jq = 0; jq < 4; ++jq) {
+          const int r0 = jq * 8 + kg * 4;
+          const float4 ls4 = *reinterpret_cast<const float4*>(sLse + r0);
+          const float4 de4 = *reinterpret_cast<const float4*>(sDel + r0);
+          const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
+          const float dev[4] = {de4.x, de4.y, de4.z, de4.w};
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + nat_rd + kk * 32);
-            const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sdO + nat_rd + kk * 32);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sacc, 0, 0, 0);
-            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], pacc, 0, 0, 0);
-          }
-          // sacc[j] = S[row (j/4)*8 + kg*4 + j%4][key n]
-          float pv[16], dsv[16];
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const int r0 = jq * 8 + kg * 4;
-            const float4 ls4 = *reinterpret_cast<const float4*>(sLse + r0);
-            const float4 de4 = *reinterpret_cast<const float4*>(sDel + r0);
-            const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
-            const float dev[4] = {de4.x, de4.y, de4.z, de4.w};
-            int4 lo4 = make_int4(0, 0, 0, 0), hi4 = make_int4(0, 0, 0, 0);
-            if (!full) {
-              lo4 = *reinterpret_cast<const int4*>(sLo + r0);
-              hi4 = *reinterpret_cast<const int4*>(sHi + r0);
-            }
-            const int lov[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
-            const int hiv[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int j = jq * 4 + e;
-              float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
-              if (!full && (key < lov[e] || key >= hiv[e])) p = 0.f;
-              pv[j] = p;
-              dsv[j] = p * (pacc[j] - dev[e]);
-            }
-          }
-          bf16x8 pb[2], dsb[2];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            pb[0][i] = static_cast<__bf16>(pv[i]);
-            pb[1][i] = static_cast<__bf16>(pv[8 + i]);
-            dsb[0][i] = static_cast<__bf16>(dsv[i]);
-            dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
-          }
-          // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, accumulator order).
-#pragma unroll
-          for (int kk2 = 0; kk2 < 2; ++kk2) {
-            const int rowb = (16 * kk2 + tr_row) * L::QP + tr_col;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const bf16x8 a_do = lds_tr_pair(sdO + rowb + db * 64, 8 * L::QP);
-              const bf16x8 a_q = lds_tr_pair(sQ + rowb + db * 64, 8 * L::QP);
-              dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_do, pb[kk2], dvacc[db], 0, 0, 0);
-              dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q, dsb[kk2], dkacc[db], 0, 0, 0);
-            }
-          }
-          // dS^T rows (this lane's key), 4 consecutive query rows per store.
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            uint2 pk;
-            pk.x = pack_bf16x2(dsv[4 * jq], dsv[4 * jq + 1]);
-            pk.y = pack_bf16x2(dsv[4 * jq + 2], dsv[4 * jq + 3]);
-            *reinterpret_cast<uint2*>(dsrow + jq * 16) = pk;
-          }
-        } else {
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) *reinterpret_cast<uint2*>(dsrow + jq * 16) = make_uint2(0, 0);
-        }
-        __syncthreads();
-        // dQ tile part: rows t0..t0+31, d block dq_db, keys dq_k0 .. +DQ_KEYS.
-        {
-          f32x16 qacc;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) qacc[j] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < DQ_KEYS / 16; ++ks) {
-            const int krow = dq_k0 + ks * 16 + tr_row;
-            const bf16x8 a_ds = lds_tr_pair(sdS + krow * L::SP + tr_col, 8 * L::SP);
-            const bf16x8 b_k = lds_tr_pair(sK + krow * L::KP + tr_col + dq_db * 64, 8 * L::KP);
-            qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ds, b_k, qacc, 0, 0, 0);
-          }
-          // qacc[j] = dQ[row (j/4)*8 + kg*4 + j%4][d = 32*dq_db + n]
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int t = t0 + (j >> 2) * 8 + kg * 4 + (j & 3);
-            if (t < s.q_len) {
-              float* dst = dq_acc + ((static_cast<int64_t>(b) * s.q_len + t) * s.h_q + h) * D +
-                           dq_db * 32 + n;
-              __hip_atomic_fetch_add(dst, qacc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+          for (int e = 0; e < 4; ++e) {
+            const int j = jq * 4 + e;
+            const unsigned rel = static_cast<unsigned>(t0 + r0 + e - mask_lo);
+            float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
+            // allowed iff qlo_k <= row < qhi_k; a select also clears inf on padding rows
+            p = rel < mask_span ? p : 0.f;
+            pv[j] = p;
+            dsv[j] = p * (pacc[j] - dev[e]);
           }
         }
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pb[0][i] = static_cast<__bf16>(pv[i]);
+        pb[1][i] = static_cast<__bf16>(pv[8 + i]);
+        dsb[0][i] = static_cast<__bf16>(dsv[i]);
+        dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
+      }
+      // dS^T row of this lane's key: 4 consecutive query rows per store.
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        uint2 pk;
+        pk.x = pack_bf16x2(dsv[4 * jq], dsv[4 * jq + 1]);
+        pk.y = pack_bf16x2(dsv[4 * jq + 2], dsv[4 * jq + 3]);
+        *reinterpret_cast<uint2*>(dsrow + ((jq ^ ksw) << 4)) = pk;
+      }
+    } else {
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) *reinterpret_cast<uint2*>(dsrow + ((jq ^ ksw) << 4)) = make_uint2(0, 0);
     }
+    // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, accumulator order).
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const int r_a = 16 * kk2 + tr_row, r_b = r_a + 8;
+      const int sw_a = qswz<D>(r_a), sw_b = qswz<D>(r_b);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
+        const int half = (tr_s & 1) * 8;
+        const int pa = r_a * L::QP + ((chunk ^ sw_a) << 4) + half;
+        const int pb_ = r_b * L::QP + ((chunk ^ sw_b) << 4) + half;
+        const bf16x8 a_do = lds_tr_pair(sdO + pa, sdO + pb_);
+        const bf16x8 a_q = lds_tr_pair(sQ + pa, sQ + pb_);
+        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_do, pb[kk2], dvacc[db], 0, 0, 0);
+        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q, dsb[kk2], dkacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // dS^T complete
+    // dQ tile part: rows t0..t0+31, d block dq_db, keys dq_k0 .. +DQ_KEYS.
+    {
+      f32x16 qacc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) qacc[j] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DQ_KEYS / 16; ++ks) {
+        const int ra = dq_k0 + ks * 16 + tr_row, rb = ra + 8;
+        const int chunk = 2 * tr_g + (tr_s >> 1), half = (tr_s & 1) * 8;
+        const bf16x8 a_ds = lds_tr_pair(sdS + ra * L::SP + ((chunk ^ ((ra >> 2) & 3)) << 4) + half,
+                                        sdS + rb * L::SP + ((chunk ^ ((rb >> 2) & 3)) << 4) + half);
+        const bf16x8 b_k = lds_tr_pair(sK + ra * L::KP + tr_col + dq_db * 64,
+                                       sK + rb * L::KP + tr_col + dq_db * 64);
+        qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ds, b_k, qacc, 0, 0, 0);
+      }
+      // qacc[j] = dQ[row t0 + (j/4)*8 + kg*4 + j%4][d = 32*dq_db + n]
+      float* base = dq_acc + (static_cast<int64_t>(b) * s.q_len * s.h_q + h) * D;
+      const int nbytes = (s.q_len * row_stride - h * D) * 4;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int soff = (t0 + (j >> 2) * 8 + (j & 3)) * row_stride * 4;
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(qacc[j], rsrc, dq_voff, soff, 0);
+      }
+    }
+    if (more) store_it(buf ^ 1);  // last read before this iteration's first barrier
+    __syncthreads();              // next buffer ready; dS^T free again
   }
   // dK, dV of this lane's key: dvacc[db][j] = dV^T[d = 32db + (j/4)*8 + kg*4 + j%4][key n]
   if (key_ok) {
@@ -355,6 +435,12 @@ hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim) {
+  // a (batch row, head)'s dQ accumulator window must be addressable with
+  // 32-bit buffer offsets
+  return q_len * h_q * head_dim * 4 < (int64_t{1} << 31);
+}
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
   return a.head_dim == 64 ? bwd_mfma_t<64>(a, st) : bwd_mfma_t<128>(a, st);

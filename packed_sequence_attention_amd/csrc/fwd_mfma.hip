@@ -44,7 +44,9 @@ template <int D>
 struct FwdLds {
   static constexpr int KP = D * 2 + 16;  // K row pitch (bytes): 16-byte skew per row
   static constexpr int VP = D * 2 + 64;  // V row pitch: rows of a transpose read hit distinct banks
-  static constexpr int bytes = kBN * (KP + VP);
+  static constexpr int buf = kBN * (KP + VP);  // one K/V tile
+  static constexpr int bytes = 2 * buf;        // double buffered
+  static constexpr int NCH = kBN * (D / 8) / 256;  // 16-byte chunks per thread per tensor
 };
 
 __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, int second_off) {
@@ -65,9 +67,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
   constexpr int KP = FwdLds<D>::KP;
   constexpr int VP = FwdLds<D>::VP;
   constexpr int CH = D / 8;   // 16-byte chunks per K/V row
+  constexpr int NCH = FwdLds<D>::NCH;
   __shared__ __attribute__((aligned(16))) char smem[FwdLds<D>::bytes];
-  char* sK = smem;
-  char* sV = smem + kBN * KP;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
@@ -121,24 +122,47 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
   const int k_rd = n * KP + kg * 16;
   const int v_rd = (4 * kg + ((lane & 15) >> 2)) * VP + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
 
+  // K/V tile staging: global -> registers (issued one tile ahead) -> LDS.
+  uint4 kx[NCH], vx[NCH];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = tid + 256 * i;
+      const int r = ci / CH, col = ci % CH;
+      const int j = kt * kBN + r;
+      kx[i] = make_uint4(0, 0, 0, 0);
+      vx[i] = make_uint4(0, 0, 0, 0);
+      if (j < s.seq_len) {
+        const int64_t off = ((static_cast<int64_t>(b) * s.seq_len + j) * s.h_kv + g) * D + col * 8;
+        kx[i] = *reinterpret_cast<const uint4*>(k + off);
+        vx[i] = *reinterpret_cast<const uint4*>(v + off);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* sK = smem + buf * FwdLds<D>::buf;
+    char* sV = sK + kBN * KP;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ci = tid + 256 * i;
+      const int r = ci / CH, col = ci % CH;
+      *reinterpret_cast<uint4*>(sK + r * KP + col * 16) = kx[i];
+      *reinterpret_cast<uint4*>(sV + r * VP + col * 16) = vx[i];
+    }
+  };
+
   if (kmax > kmin) {
     const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
+    load_tile(kt0);
+    store_tile(0);
+    __syncthreads();
     for (int kt = kt0; kt <= kt1; ++kt) {
+      const int buf = (kt - kt0) & 1;
+      const bool more = kt < kt1;
+      if (more) load_tile(kt + 1);  // in flight during this tile's math
+      const char* sK = smem + buf * FwdLds<D>::buf;
+      const char* sV = sK + kBN * KP;
       const int k0 = kt * kBN;
-      __syncthreads();
-      for (int ci = tid; ci < kBN * CH; ci += 256) {
-        const int r = ci / CH, col = ci % CH;
-        const int j = k0 + r;
-        uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
-        if (j < s.seq_len) {
-          const int64_t off = ((static_cast<int64_t>(b) * s.seq_len + j) * s.h_kv + g) * D + col * 8;
-          kx = *reinterpret_cast<const uint4*>(k + off);
-          vx = *reinterpret_cast<const uint4*>(v + off);
-        }
-        *reinterpret_cast<uint4*>(sK + r * KP + col * 16) = kx;
-        *reinterpret_cast<uint4*>(sV + r * VP + col * 16) = vx;
-      }
-      __syncthreads();
       const bool full = all_real && lomax <= k0 && k0 + kBN - 1 <= pfirst;
 #pragma unroll
       for (int sb = 0; sb < kBN / 32; ++sb) {
@@ -197,6 +221,8 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
           }
         }
       }
+      if (more) store_tile(buf ^ 1);  // that buffer was last read before the previous barrier
+      __syncthreads();
     }
   }
 

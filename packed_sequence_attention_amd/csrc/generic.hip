@@ -263,35 +263,48 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
   }
 }
 
-// One thread per (b, local row, query head): delta = sum_d dO * O in float32;
-// also zeroes that row of the float32 dQ accumulator when one is given.
+// delta = sum_d dO * O in float32 for every (b, local row, query head), and
+// (when given) zero that row of the float32 dQ accumulator.  A group of lpr
+// lanes (a power of two >= head_dim / 8) handles one row with 16-byte
+// accesses, so consecutive lanes touch consecutive memory.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnShape s, const T* __restrict__ o,
                                                        const T* __restrict__ d_o,
                                                        float* __restrict__ delta,
-                                                       float* __restrict__ dq_acc) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+                                                       float* __restrict__ dq_acc, int lpr) {
+  const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t idx = gtid / lpr;  // row (b, t, h), h fastest
+  const int sub = static_cast<int>(gtid % lpr);
   const int64_t total = static_cast<int64_t>(s.batch) * s.q_len * s.h_q;
-  if (idx >= total) return;
   const int D = s.head_dim;
-  const int h = static_cast<int>(idx % s.h_q);
-  const int64_t bt = idx / s.h_q;
-  const int t = static_cast<int>(bt % s.q_len);
-  const int b = static_cast<int>(bt / s.q_len);
-  const int64_t row = idx * D;
+  const bool in = idx < total && sub * 8 < D;
   float acc = 0.f;
-  for (int d = 0; d < D; d += 8) {
+  if (in) {
     float x[8], y[8];
-    load8(o + row + d, x);
-    load8(d_o + row + d, y);
+    load8(o + idx * D + sub * 8, x);
+    load8(d_o + idx * D + sub * 8, y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
+    if (dq_acc != nullptr) {
+      float4* z = reinterpret_cast<float4*>(dq_acc + idx * D + sub * 8);
+      z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
-  delta[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t] = acc;
-  if (dq_acc != nullptr) {
-    float4* z = reinterpret_cast<float4*>(dq_acc + row);
-    for (int d = 0; d < D / 4; ++d) z[d] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int off = lpr >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (sub == 0 && idx < total) {
+    const int h = static_cast<int>(idx % s.h_q);
+    const int64_t bt = idx / s.h_q;
+    const int t = static_cast<int>(bt % s.q_len);
+    const int b = static_cast<int>(bt / s.q_len);
+    delta[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t] = acc;
   }
+}
+
+int lanes_per_row(int head_dim) {
+  int l = 1;
+  while (l < head_dim / 8) l <<= 1;
+  return l;
 }
 
 AttnShape make_shape(int batch, int seq_len, int row_offset, int q_len, int h_q, int h_kv,
@@ -324,8 +337,9 @@ hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
   AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
-  bwd_prep_kernel<T><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, st>>>(
-      s, static_cast<const T*>(a.o), static_cast<const T*>(a.d_o), a.delta, nullptr);
+  const int lpr = lanes_per_row(a.head_dim);
+  bwd_prep_kernel<T><<<static_cast<unsigned>((rows * lpr + 255) / 256), 256, 0, st>>>(
+      s, static_cast<const T*>(a.o), static_cast<const T*>(a.d_o), a.delta, nullptr, lpr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dq_generic_kernel<T, NR><<<blocks_for(rows), 256, 0, st>>>(
@@ -382,12 +396,14 @@ hipError_t launch_zero_u16(void* p, int64_t n, hipStream_t st) {
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
   AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
   const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
+  const int lpr = lanes_per_row(a.head_dim);
+  const unsigned grid = static_cast<unsigned>((rows * lpr + 255) / 256);
   if (a.dtype == 0)
-    bwd_prep_kernel<float><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, st>>>(
-        s, static_cast<const float*>(a.o), static_cast<const float*>(a.d_o), a.delta, a.dq_acc);
+    bwd_prep_kernel<float><<<grid, 256, 0, st>>>(s, static_cast<const float*>(a.o),
+                                                 static_cast<const float*>(a.d_o), a.delta, a.dq_acc, lpr);
   else
-    bwd_prep_kernel<uint16_t><<<static_cast<unsigned>((rows + 255) / 256), 256, 0, st>>>(
-        s, static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.d_o), a.delta, a.dq_acc);
+    bwd_prep_kernel<uint16_t><<<grid, 256, 0, st>>>(s, static_cast<const uint16_t*>(a.o),
+                                                    static_cast<const uint16_t*>(a.d_o), a.delta, a.dq_acc, lpr);
   return hipGetLastError();
 }
 

@@ -55,6 +55,9 @@ hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t stream);
 bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
+// The matrix-core backward addresses one (batch row, head)'s float32 dQ
+// accumulator rows with 32-bit buffer offsets.
+bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim);
 
 // Backward row statistics: delta = rowsum(dO * O) in float32, and (if
 // dq_acc is non-null) zero the float32 dQ accumulator.
