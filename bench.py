@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (3 launches): a known-size "
+                         "reference for HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU's share only: run it with --gpus 1 (the multi-GPU exchange "
@@ -165,6 +168,13 @@ def main():
     flops_bwd = 10 * D * Hq * pairs
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev)
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib * (1 << 20) // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(marks=None):
         seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device=dev)
