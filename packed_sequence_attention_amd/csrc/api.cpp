@@ -7,7 +7,7 @@
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 
-#include "../../include/blockdiag.h"
+#include "blockdiag.h"
 #include "internal.h"
 #include "launch.h"
 

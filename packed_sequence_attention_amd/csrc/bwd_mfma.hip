@@ -34,8 +34,9 @@
 //   row read and 4 rows x 4 chunks of a transpose read all land on distinct
 //   banks.  K tile: rows padded by 64 bytes.  dS^T: 64-byte rows with the
 //   chunk index xor-ed by bits 2..3 of the row.
-// Q / dO / LSE / delta of the next query tile are loaded into registers
-// while the current one is processed (LDS double buffer).
+// Q / dO / LSE / delta of the next query tile are loaded straight into the
+// other half of an LDS double buffer (LDS-DMA) while the current one is
+// processed.
 #include <limits.h>
 #include <math.h>
 
@@ -53,13 +54,13 @@ struct BwdLds {
   static constexpr int KP = D * 2 + 64;  // K tile row pitch (transpose loads)
   static constexpr int QP = D * 2;       // Q / dO tile row pitch (xor-swizzled chunks)
   static constexpr int SP = kQB * 2;     // dS^T row pitch (32 bf16)
-  static constexpr int stat = 2 * kQB * 4;          // lse * log2(e), delta
+  static constexpr int stat = 2 * kQB * 4;          // lse, delta
   static constexpr int qbuf = 2 * kQB * QP + stat;  // one Q/dO/statistics buffer
   static constexpr int off_q = kKB * KP;            // two qbuf follow the K tile
   static constexpr int off_ds = off_q + 2 * qbuf;
-  static constexpr int off_red = off_ds + kKB * SP;
+  static constexpr int off_red = off_ds + 2 * kKB * SP;  // two dS^T buffers
   static constexpr int bytes = off_red + 16 * 4;
-  static constexpr int NCH = kQB * (D / 8) / 256;   // 16-byte chunks per thread per tensor
+  static constexpr int NCH = kQB * (D / 8) / 256;   // 16-byte direct loads per thread per tensor
 };
 
 // Chunk swizzle of row r of a Q / dO tile (see the file comment).
@@ -126,6 +127,10 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
           k + ((static_cast<int64_t>(b) * s.seq_len + j) * s.h_kv + g) * D + col * 8);
     *reinterpret_cast<uint4*>(sK + r * L::KP + col * 16) = x;
   }
+  // Both dS^T buffers start at zero (the first iteration's deferred dQ
+  // product reads one of them).
+  for (int i = tid; i < 2 * kKB * L::SP / 16; i += 256)
+    reinterpret_cast<uint4*>(sdS)[i] = make_uint4(0, 0, 0, 0);
   // Local rows attending this lane's key: [qlo_k, qhi_k) (empty: qlo_k >= qhi_k).
   int qlo_k = INT_MAX, qhi_k = INT_MIN;
   if (key_ok) {
@@ -137,8 +142,6 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
     }
   }
   const int wqlo = wave_min_i(qlo_k), wqhi = wave_max_i(qhi_k);
-  // Rows every key of the wave attends: [wfull_lo, wfull_hi).
-  const int wfull_lo = wave_max_i(qlo_k), wfull_hi = wave_min_i(qhi_k);
   // Element mask: row t is allowed iff (unsigned)(t - mask_lo) < mask_span.
   const int mask_lo = qhi_k > qlo_k ? qlo_k : 0;
   const unsigned mask_span = qhi_k > qlo_k ? static_cast<unsigned>(qhi_k - qlo_k) : 0u;
@@ -172,88 +175,112 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
   const int row_stride = s.h_q * D;  // elements between consecutive rows
   const int dq_voff = ((kg * 4) * row_stride + dq_db * 32 + n) * 4;
 
-  // Q / dO / statistics staging: global -> registers (one iteration ahead)
-  // -> LDS double buffer.  Iteration it covers query head g*group + it / n_q
-  // and the query tile qt0 + it % n_q.
-  uint4 qx[NCH], ox[NCH];
-  float st_lse = 0.f, st_del = 0.f;
+  // Q / dO / statistics staging: direct global -> LDS loads (buffer form,
+  // so rows past the chunk read as zero) into an LDS double buffer, issued
+  // one iteration ahead.  Iteration it covers query head g*group + it / n_q
+  // and the query tile qt0 + it % n_q.  Q / dO land in the swizzled layout:
+  // lane l of a load writes LDS chunk (base + l), so each lane fetches the
+  // global chunk that belongs at that position.
   const int qt0 = gqlo / kQB;
   const int n_q = gqhi > gqlo ? (gqhi - 1) / kQB - qt0 + 1 : 0;
   const int n_it = n_q * s.group;
-  auto load_it = [&](int it) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto issue_loads = [&](int it, int buf) {
     const int h = g * s.group + it / n_q;
     const int t0 = (qt0 + it % n_q) * kQB;
+    const int64_t head0 = (static_cast<int64_t>(b) * s.q_len * s.h_q + h) * D;  // row 0 of (b, h)
+    const int nbytes = (s.q_len * row_stride - h * D) * 2;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(q + head0), 0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(d_o + head0), 0, nbytes, 0x00020000);
+    char* sQb = smem + L::off_q + buf * L::qbuf;
+    char* sdOb = sQb + kQB * L::QP;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CH, col = ci % CH;
-      const int t = t0 + r;
-      qx[i] = make_uint4(0, 0, 0, 0);
-      ox[i] = make_uint4(0, 0, 0, 0);
-      if (t < s.q_len) {
-        const int64_t off = ((static_cast<int64_t>(b) * s.q_len + t) * s.h_q + h) * D + col * 8;
-        qx[i] = *reinterpret_cast<const uint4*>(q + off);
-        ox[i] = *reinterpret_cast<const uint4*>(d_o + off);
-      }
+      const int lc = i * 256 + tid;  // LDS chunk written by this lane
+      const int r = lc / CH, pchunk = lc % CH;
+      const int c = pchunk ^ qswz<D>(r);
+      const int voff = ((t0 + r) * row_stride + c * 8) * 2;
+      const int lbase = (i * 256 + wave * 64) * 16;  // wave-uniform LDS destination
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sQb + lbase), 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void*)(sdOb + lbase), 16, voff, 0, 0, 0);
     }
-    if (tid < kQB) {
-      const int t = t0 + tid;
-      st_lse = 0.f;
-      st_del = 0.f;
-      if (t < s.q_len) {  // padding rows (LSE = -inf) are masked out later
-        const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
-        st_lse = lse[st];
-        st_del = delta[st];
-      }
-    }
-  };
-  auto store_it = [&](int buf) {
-    char* sQ = smem + L::off_q + buf * L::qbuf;
-    char* sdO = sQ + kQB * L::QP;
-    float* stat = reinterpret_cast<float*>(sdO + kQB * L::QP);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CH, col = ci % CH;
-      const int pos = r * L::QP + ((col ^ qswz<D>(r)) << 4);
-      *reinterpret_cast<uint4*>(sQ + pos) = qx[i];
-      *reinterpret_cast<uint4*>(sdO + pos) = ox[i];
-    }
-    if (tid < kQB) {
-      stat[tid] = st_lse * kLog2e;
-      stat[kQB + tid] = st_del;
+    if (wave == 0) {  // LSE to stat[0..31], delta to stat[32..63]
+      char* stat = sdOb + kQB * L::QP;
+      const int64_t st0 = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len;
+      const int sbytes = s.q_len * 4;
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(lse + st0), 0, sbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(delta + st0), 0, sbytes, 0x00020000);
+      if (lane < kQB)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)stat, 4, (t0 + lane) * 4, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)stat, 4, (t0 + lane - kQB) * 4, 0, 0, 0);
     }
   };
 
+  // dQ of one finished tile: rows tt0..tt0+31 of head hh, d block dq_db, keys
+  // dq_k0 .. +DQ_KEYS of this workgroup, from dS^T in LDS; float32 atomics.
+  auto dq_tile = [&](const char* dsbuf, int hh, int tt0) {
+    f32x16 qacc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qacc[j] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DQ_KEYS / 16; ++ks) {
+      const int ra = dq_k0 + ks * 16 + tr_row, rb = ra + 8;
+      const int chunk = 2 * tr_g + (tr_s >> 1), half = (tr_s & 1) * 8;
+      const bf16x8 a_ds = lds_tr_pair(dsbuf + ra * L::SP + ((chunk ^ ((ra >> 2) & 3)) << 4) + half,
+                                      dsbuf + rb * L::SP + ((chunk ^ ((rb >> 2) & 3)) << 4) + half);
+      const bf16x8 b_k = lds_tr_pair(sK + ra * L::KP + tr_col + dq_db * 64,
+                                     sK + rb * L::KP + tr_col + dq_db * 64);
+      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ds, b_k, qacc, 0, 0, 0);
+    }
+    // qacc[j] = dQ[row tt0 + (j/4)*8 + kg*4 + j%4][d = 32*dq_db + n]
+    float* base = dq_acc + (static_cast<int64_t>(b) * s.q_len * s.h_q + hh) * D;
+    const int nbytes = (s.q_len * row_stride - hh * D) * 4;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int soff = (tt0 + (j >> 2) * 8 + (j & 3)) * row_stride * 4;
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(qacc[j], rsrc, dq_voff, soff, 0);
+    }
+  };
+
+  // Software pipeline, one barrier per iteration.  Iteration it: the dQ
+  // product of tile it-1 (its dS^T is complete in the other dS^T buffer) and
+  // its atomics; the direct loads of tile it+1 into the other Q/dO buffer;
+  // S, dP, the softmax, dS^T and the dV/dK products of tile it; then a wait
+  // for all outstanding memory operations and the barrier.  The dQ product of
+  // the last tile follows the loop.
+  const int krow = wave * 32 + n;
+  const int ksw = (krow >> 2) & 3;
   if (n_it > 0) {
-    load_it(0);
-    store_it(0);
+    issue_loads(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  int prev_h = g * s.group, prev_t0 = qt0 * kQB;
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
-    const bool more = it + 1 < n_it;
-    if (more) load_it(it + 1);  // in flight during this iteration's math
     const int h = g * s.group + it / n_q;
     const int t0 = (qt0 + it % n_q) * kQB;
     const char* sQ = smem + L::off_q + buf * L::qbuf;
     const char* sdO = sQ + kQB * L::QP;
     const float* sLse = reinterpret_cast<const float*>(sdO + kQB * L::QP);
     const float* sDel = sLse + kQB;
-    const bool active = wqlo < t0 + kQB && wqhi > t0;
-    const int krow = wave * 32 + n;
-    char* dsrow = sdS + krow * L::SP + kg * 8;
-    const int ksw = (krow >> 2) & 3;
-    // P and dS as bf16 B operands (k = query rows in accumulator order);
-    // zero on waves whose keys no row of this tile attends, so the dV / dK
-    // products below run unconditionally and their accumulators stay put.
-    bf16x8 pb[2], dsb[2];
+    char* ds_cur = sdS + buf * (kKB * L::SP);
+    const char* ds_prev = sdS + (buf ^ 1) * (kKB * L::SP);
+
+    // dQ of the previous tile (for it == 0: an all-zero dS^T buffer).
+    dq_tile(ds_prev, prev_h, prev_t0);
+    if (it + 1 < n_it) issue_loads(it + 1, buf ^ 1);  // that buffer was last read before the last barrier
+
+    f32x16 sacc, pacc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pb[0][i] = pb[1][i] = dsb[0][i] = dsb[1][i] = static_cast<__bf16>(0.f);
-    if (active) {
-      f32x16 sacc, pacc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
+    for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
+    {
       const int nat_row = n * L::QP;
       const int nat_swz = qswz<D>(n);
 #pragma unroll
@@ -264,63 +291,43 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], pacc, 0, 0, 0);
       }
-      // sacc[j] = S[row (j/4)*8 + kg*4 + j%4][key n]
-      float dsv[16];
-      float pv[16];
-      // every (row, key) pair of this 32x32 block allowed?  (uniform branch)
-      if (wfull_lo <= t0 && t0 + kQB <= wfull_hi) {
+    }
+    // sacc[j] = S[row t0 + (j/4)*8 + kg*4 + j%4][key n].  P is zero outside
+    // the mask, which also covers padding rows, rows past the chunk and
+    // waves whose keys no row of this tile attends.
+    float pv[16], dsv[16];
 #pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const int r0 = jq * 8 + kg * 4;
-          const float4 ls4 = *reinterpret_cast<const float4*>(sLse + r0);
-          const float4 de4 = *reinterpret_cast<const float4*>(sDel + r0);
-          const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
-          const float dev[4] = {de4.x, de4.y, de4.z, de4.w};
+    for (int jq = 0; jq < 4; ++jq) {
+      const int r0 = jq * 8 + kg * 4;
+      const float4 ls4 = *reinterpret_cast<const float4*>(sLse + r0);
+      const float4 de4 = *reinterpret_cast<const float4*>(sDel + r0);
+      const float lsv[4] = {ls4.x * kLog2e, ls4.y * kLog2e, ls4.z * kLog2e, ls4.w * kLog2e};
+      const float dev[4] = {de4.x, de4.y, de4.z, de4.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = jq * 4 + e;
-            pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
-            dsv[j] = pv[j] * (pacc[j] - dev[e]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const int r0 = jq * 8 + kg * 4;
-          const float4 ls4 = *reinterpret_cast<const float4*>(sLse + r0);
-          const float4 de4 = *reinterpret_cast<const float4*>(sDel + r0);
-          const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
-          const float dev[4] = {de4.x, de4.y, de4.z, de4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = jq * 4 + e;
-            const unsigned rel = static_cast<unsigned>(t0 + r0 + e - mask_lo);
-            float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
-            // allowed iff qlo_k <= row < qhi_k; a select also clears inf on padding rows
-            p = rel < mask_span ? p : 0.f;
-            pv[j] = p;
-            dsv[j] = p * (pacc[j] - dev[e]);
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int j = jq * 4 + e;
+        const unsigned rel = static_cast<unsigned>(t0 + r0 + e - mask_lo);
+        float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
+        p = rel < mask_span ? p : 0.f;  // a select: also clears inf on padding rows
+        pv[j] = p;
+        dsv[j] = p * (pacc[j] - dev[e]);
       }
+    }
+    bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pb[0][i] = static_cast<__bf16>(pv[i]);
-        pb[1][i] = static_cast<__bf16>(pv[8 + i]);
-        dsb[0][i] = static_cast<__bf16>(dsv[i]);
-        dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
-      }
-      // dS^T row of this lane's key: 4 consecutive query rows per store.
+    for (int i = 0; i < 8; ++i) {
+      pb[0][i] = static_cast<__bf16>(pv[i]);
+      pb[1][i] = static_cast<__bf16>(pv[8 + i]);
+      dsb[0][i] = static_cast<__bf16>(dsv[i]);
+      dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
+    }
+    // dS^T row of this lane's key: 4 consecutive query rows per store.
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        uint2 pk;
-        pk.x = pack_bf16x2(dsv[4 * jq], dsv[4 * jq + 1]);
-        pk.y = pack_bf16x2(dsv[4 * jq + 2], dsv[4 * jq + 3]);
-        *reinterpret_cast<uint2*>(dsrow + ((jq ^ ksw) << 4)) = pk;
-      }
-    } else {
-#pragma unroll
-      for (int jq = 0; jq < 4; ++jq) *reinterpret_cast<uint2*>(dsrow + ((jq ^ ksw) << 4)) = make_uint2(0, 0);
+    for (int jq = 0; jq < 4; ++jq) {
+      uint2 pk;
+      pk.x = pack_bf16x2(dsv[4 * jq], dsv[4 * jq + 1]);
+      pk.y = pack_bf16x2(dsv[4 * jq + 2], dsv[4 * jq + 3]);
+      *reinterpret_cast<uint2*>(ds_cur + krow * L::SP + ((jq ^ ksw) << 4) + kg * 8) = pk;
     }
     // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, accumulator order).
 #pragma unroll
@@ -339,35 +346,13 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
         dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q, dsb[kk2], dkacc[db], 0, 0, 0);
       }
     }
-    __syncthreads();  // dS^T complete
-    // dQ tile part: rows t0..t0+31, d block dq_db, keys dq_k0 .. +DQ_KEYS.
-    {
-      f32x16 qacc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) qacc[j] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DQ_KEYS / 16; ++ks) {
-        const int ra = dq_k0 + ks * 16 + tr_row, rb = ra + 8;
-        const int chunk = 2 * tr_g + (tr_s >> 1), half = (tr_s & 1) * 8;
-        const bf16x8 a_ds = lds_tr_pair(sdS + ra * L::SP + ((chunk ^ ((ra >> 2) & 3)) << 4) + half,
-                                        sdS + rb * L::SP + ((chunk ^ ((rb >> 2) & 3)) << 4) + half);
-        const bf16x8 b_k = lds_tr_pair(sK + ra * L::KP + tr_col + dq_db * 64,
-                                       sK + rb * L::KP + tr_col + dq_db * 64);
-        qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ds, b_k, qacc, 0, 0, 0);
-      }
-      // qacc[j] = dQ[row t0 + (j/4)*8 + kg*4 + j%4][d = 32*dq_db + n]
-      float* base = dq_acc + (static_cast<int64_t>(b) * s.q_len * s.h_q + h) * D;
-      const int nbytes = (s.q_len * row_stride - h * D) * 4;
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int soff = (t0 + (j >> 2) * 8 + (j & 3)) * row_stride * 4;
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(qacc[j], rsrc, dq_voff, soff, 0);
-      }
-    }
-    if (more) store_it(buf ^ 1);  // last read before this iteration's first barrier
-    __syncthreads();              // next buffer ready; dS^T free again
+    prev_h = h;
+    prev_t0 = t0;
+    __builtin_amdgcn_s_waitcnt(0);  // direct loads of tile it+1 have landed in LDS
+    __syncthreads();                // dS^T of this tile complete; next Q/dO buffer ready
   }
+  if (n_it > 0) dq_tile(sdS + (n_it & 1 ? 0 : 1) * (kKB * L::SP), prev_h, prev_t0);
+
   // dK, dV of this lane's key: dvacc[db][j] = dV^T[d = 32db + (j/4)*8 + kg*4 + j%4][key n]
   if (key_ok) {
     uint16_t* dkr = dk + kv_row * D + kg * 4;

@@ -1,7 +1,7 @@
 // Internal helpers of the C ABI layer: thread-local error message.
 #pragma once
 
-#include "../../include/blockdiag.h"
+#include "blockdiag.h"
 
 namespace bd {
 // Records a formatted message for blockdiag_last_error() and returns code.

@@ -18,7 +18,7 @@
 
 #include <string>
 
-#include "../../include/blockdiag.h"
+#include "blockdiag.h"
 #include "internal.h"
 
 namespace bd {
