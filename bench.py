@@ -13,10 +13,13 @@ workload is bf16 B=2, S=4096 per row, H_q=32, H_kv=8, d=128, lognormal
 document lengths (median 512), row_offset 0.
 
 Printed: one JSON line (rank 0), with
-  roofline      the backward's main kernel (the dominant one): algorithmic
-                FLOP per launch / its mean duration from HIP events recorded
-                around that kernel on its stream, against the bf16 dense
-                matrix-core peak; `traffic` from the committed rocprofv3
+  roofline      the backward's dK/dV kernel (the dominant one): algorithmic
+                FLOP per launch (the four products S, dP, dV, dK at 2*d FLOP
+                per allowed pair and query head each; the backward's fifth,
+                dQ, is credited to the dQ kernel and its recomputation of S
+                and dP is not counted) / its mean duration from HIP events
+                recorded around that kernel on its stream, against the bf16
+                dense matrix-core peak; `traffic` from the committed rocprofv3
                 counter summary when it was taken on the current kernel
                 source, else null;
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
@@ -224,7 +227,8 @@ def main():
     tb = float(np.median(times_b))
 
     value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
-    achieved = flops_bwd / (bwd_avg * 1e-3) / 1e12
+    flops_dkdv = 8 * D * Hq * pairs
+    achieved = flops_dkdv / (bwd_avg * 1e-3) / 1e12
     traffic = traffic_from_profile("bwd_mfma.hip", f"w{args.workload}") if w.dtype == "bf16" else None
     out = {
         "metric": METRIC,
@@ -245,9 +249,9 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_bwd_entry_ms": {"fwd": round(tf, 4), "bwd": round(tb, 4)},
         "tflops_fwd_plus_bwd_calls": round((flops_fwd + flops_bwd) / ((tf + tb) * 1e-3) / 1e12, 3),
-        "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd": round(bwd_avg, 4)},
+        "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd_dkdv": round(bwd_avg, 4)},
         "fwd_kernel_tflops": round(flops_fwd / (fwd_avg * 1e-3) / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": "bwd_mfma_kernel", "achieved": round(achieved, 3),
+        "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_kernel", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }

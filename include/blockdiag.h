@@ -188,9 +188,9 @@ bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
  *   gives the full gradient (Design overview, exchange.py: the K/V gradient
  *   is reduce-scattered with SUM).
  *   workspace: at least blockdiag_workspace_bytes(1, ...) bytes of device
- *   memory (float32 row statistics and a float32 dQ accumulator).
- * The dK/dV result is deterministic; dQ is accumulated with float32 atomics
- * on matrix-core paths, so its last bits may differ run to run.
+ *   memory (the float32 row statistic delta = rowsum(dO * O)).
+ * The backward is bitwise deterministic (no atomics): each of dQ, dK, dV is
+ * written once by the workgroup that owns its rows or keys.
  * Errors: as blockdiag_attn_fwd.
  */
 bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,

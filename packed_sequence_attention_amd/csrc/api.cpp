@@ -44,6 +44,11 @@ bool use_mfma_bwd(bd_dtype dtype, int32_t q_len, int32_t head_dim, int32_t h_q, 
   return use_mfma(dtype, head_dim, h_q, h_kv, scale) && bd::bwd_mfma_fits(q_len, h_q, head_dim);
 }
 
+bool use_mfma_bwd_full(bd_dtype dtype, int32_t seq_len, int32_t q_len, int32_t head_dim, int32_t h_q,
+                       int32_t h_kv, float scale) {
+  return use_mfma_bwd(dtype, q_len, head_dim, h_q, h_kv, scale) && bd::bwd_dq_fits(seq_len, h_kv, head_dim);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 thread_local hipEvent_t g_mark_start = nullptr;
@@ -93,12 +98,10 @@ extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, int32_t n_seg,
 
 extern "C" size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int32_t seq_len,
                                             int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim) {
-  (void)seq_len;
+  (void)dtype; (void)seq_len; (void)h_kv;
   if (!is_bwd || batch <= 0 || q_len <= 0 || h_q <= 0 || head_dim <= 0) return 0;
   const size_t rows = static_cast<size_t>(batch) * q_len * h_q;
-  size_t bytes = align256(rows * sizeof(float));  // delta
-  if (use_mfma_bwd(dtype, q_len, head_dim, h_q, h_kv, 1.f)) bytes += align256(rows * head_dim * sizeof(float));
-  return bytes;
+  return align256(rows * sizeof(float));  // delta
 }
 
 extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
@@ -148,13 +151,9 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
     if (e != hipSuccess) return fail(BD_ERR_HIP, "zero-fill: %s", hipGetErrorString(e));
     return BD_OK;
   }
-  const size_t rows = static_cast<size_t>(batch) * q_len * h_q;
-  char* ws = static_cast<char*>(workspace);
-  const bool mf = use_mfma_bwd(dtype, q_len, head_dim, h_q, h_kv, scale);
+  const bool mf = use_mfma_bwd_full(dtype, seq_len, q_len, head_dim, h_q, h_kv, scale);
   bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
-                q, k, v, o, lse, d_o, d_meta, dq, dk, dv,
-                reinterpret_cast<float*>(ws),
-                mf ? reinterpret_cast<float*>(ws + align256(rows * sizeof(float))) : nullptr, nullptr, nullptr};
+                q, k, v, o, lse, d_o, d_meta, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

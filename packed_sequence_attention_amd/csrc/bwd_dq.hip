@@ -1,0 +1,257 @@
+// bf16 matrix-core dQ kernel of the block-diagonal packed attention backward
+// for gfx950 (query-stationary).
+//
+// Automodel page "feat(distributed): block-diagonal varlen CP for packed
+// sequences", Proof section (input gradients).  For each local row i:
+//   P_ij  = exp(scale q_i.k_j - LSE_i),  dP_ij = dO_i . v_j,
+//   dS_ij = P_ij (dP_ij - delta_i),      dQ_i = scale sum_j dS_ij k_j
+// over the keys j of row i's document up to i.
+//
+// Work decomposition mirrors the forward: a workgroup is (batch row, 4 query
+// heads sharing one K/V head, 32 local rows); wave w owns head 4*hg + w for
+// those rows and keeps its Q and dO rows (B operands), LSE, delta and the
+// dQ^T accumulator in registers.  Key tiles of 64 are streamed through an
+// LDS double buffer with direct global -> LDS loads (buffer form: keys past
+// the row read as zero); only tiles in [doc_start(first row), last row] are
+// visited and the mask is applied only on tiles not entirely allowed.  Per
+// 32-key block (v_mfma_f32_32x32x16_bf16, lane l: query row l % 32):
+//   S^T  = K Q^T    (A = K rows from LDS, B = Q in registers)
+//   dP^T = V dO^T   (A = V rows from LDS, B = dO in registers)
+//   dS^T = P^T (dP^T - delta) in the accumulator layout, rounded to bf16
+//   dQ^T += K^T dS^T  (A = K^T with the LDS transpose load, B = dS^T)
+// K / V tiles are stored without padding with the 16-byte chunk c of row r
+// at chunk c ^ f(r); f makes both the row reads (16 rows, one chunk) and the
+// transpose reads (4 rows x 4 chunks) free of bank conflicts.  No atomics:
+// dQ is written once, deterministically.
+#include <limits.h>
+#include <math.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bd {
+namespace {
+
+constexpr int kBN = 64;  // keys per tile
+constexpr int kBM = 32;  // query rows per workgroup
+
+template <int D>
+struct DqLds {
+  static constexpr int RP = D * 2;                  // row pitch (bytes), swizzled chunks
+  static constexpr int tile = 2 * kBN * RP;         // K tile then V tile
+  static constexpr int bytes = 2 * tile;            // double buffered
+  static constexpr int NCH = kBN * (D / 8) / 256;   // direct loads per thread per tensor
+};
+
+template <int D>
+__device__ __forceinline__ int rswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  const auto ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ delta, MetaView m, uint16_t* __restrict__ dq, int n_qt, int n_hg) {
+  constexpr int KK = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int CH = D / 8;
+  using L = DqLds<D>;
+  constexpr int RP = L::RP;
+  __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, kg = lane >> 5;
+
+  // Longest-first: the last query tiles of a row have the longest key ranges.
+  const int per_qt = s.batch * n_hg;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+  const int rem = static_cast<int>(blockIdx.x) % per_qt;
+  const int b = rem / n_hg, hg = rem % n_hg;
+  const int h = hg * 4 + wave;
+  const int g = (hg * 4) / s.group;
+
+  const int t = qt * kBM + n;
+  const bool valid = t < s.q_len;
+  const int64_t bt = static_cast<int64_t>(b) * s.q_len + t;
+  int lo = 0, hi = 0;
+  float lse2 = 0.f, dlt = 0.f;
+  if (valid) {
+    lo = m.row_lo[bt];
+    hi = m.row_hi[bt];
+    const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
+    lse2 = lse[st] * kLog2e;  // -inf on padding rows: masked below
+    dlt = delta[st];
+  }
+  const bool real = hi > lo;
+  const int kmin = wave_min_i(real ? lo : INT_MAX);
+  const int kmax = wave_max_i(real ? hi : 0);
+  const int lomax = wave_max_i(real ? lo : 0);
+  const bool all_real = wave_min_i(real ? 1 : 0) == 1;
+  const int pfirst = s.row_offset + qt * kBM;
+
+  bf16x8 qf[KK], of[KK];
+  {
+    const int64_t row = (bt * s.h_q + h) * D + kg * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (valid) {
+        qf[kk] = *reinterpret_cast<const bf16x8*>(q + row + kk * 16);
+        of[kk] = *reinterpret_cast<const bf16x8*>(d_o + row + kk * 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[kk][i] = of[kk][i] = static_cast<__bf16>(0.f);
+      }
+    }
+  }
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dqacc[db][j] = 0.f;
+  const float c = s.scale * kLog2e;
+
+  // Direct loads of key tile kt into buffer buf (keys past the row read 0).
+  const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
+  const int kv_stride = s.h_kv * D;
+  const int kv_bytes = (s.seq_len * kv_stride - g * D) * 2;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + kv0), 0, kv_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + kv0), 0, kv_bytes, 0x00020000);
+  auto issue_tile = [&](int kt, int buf) {
+    char* sK = smem + buf * L::tile;
+    char* sV = sK + kBN * RP;
+#pragma unroll
+    for (int i = 0; i < L::NCH; ++i) {
+      const int lc = i * 256 + tid;  // LDS chunk written by this lane
+      const int r = lc / CH, pc = lc % CH;
+      const int cch = pc ^ rswz<D>(r);
+      const int voff = ((kt * kBN + r) * kv_stride + cch * 8) * 2;
+      const int lbase = (i * 256 + wave * 64) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sK + lbase), 16, voff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sV + lbase), 16, voff, 0, 0, 0);
+    }
+  };
+
+  const int nat_swz = rswz<D>(n);
+  const int tr_row = 4 * kg + ((lane & 15) >> 2);
+  const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
+
+  if (kmax > kmin) {
+    const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
+    issue_tile(kt0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = kt0; kt <= kt1; ++kt) {
+      const int buf = (kt - kt0) & 1;
+      if (kt < kt1) issue_tile(kt + 1, buf ^ 1);  // that buffer was last read before the last barrier
+      const char* sK = smem + buf * L::tile;
+      const char* sV = sK + kBN * RP;
+      const int k0 = kt * kBN;
+      const bool full = all_real && lomax <= k0 && k0 + kBN - 1 <= pfirst;
+#pragma unroll
+      for (int sb = 0; sb < kBN / 32; ++sb) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
+        const int rown = sb * 32 + n;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const int pos = rown * RP + (((2 * kk + kg) ^ nat_swz) << 4);
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + pos);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(sV + pos);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], pacc, 0, 0, 0);
+        }
+        // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
+        float dsv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lse2));
+          if (!full) {
+            const int key = k0 + sb * 32 + (j >> 2) * 8 + kg * 4 + (j & 3);
+            p = (key >= lo && key < hi) ? p : 0.f;  // a select: also clears inf on padding rows
+          }
+          dsv[j] = p * (pacc[j] - dlt);
+        }
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dsb[0][i] = static_cast<__bf16>(dsv[i]);
+          dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
+        }
+        // dQ^T += K^T dS^T: A = K^T (rows = keys in accumulator order).
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2) {
+          const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
+          const int swa = rswz<D>(ra), swb = rswz<D>(rb);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
+            const int half = (tr_s & 1) * 8;
+            const bf16x8 a_k = lds_tr_pair(sK + ra * RP + ((chunk ^ swa) << 4) + half,
+                                           sK + rb * RP + ((chunk ^ swb) << 4) + half);
+            dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k, dsb[kk2], dqacc[db], 0, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
+      __syncthreads();
+    }
+  }
+
+  // dqacc[db][j] = dQ^T[d = 32db + (j/4)*8 + kg*4 + j%4][row n]
+  if (valid) {
+    uint16_t* drow = dq + (bt * s.h_q + h) * D + kg * 4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        uint2 pk;
+        pk.x = pack_bf16x2(dqacc[db][4 * jq] * s.scale, dqacc[db][4 * jq + 1] * s.scale);
+        pk.y = pack_bf16x2(dqacc[db][4 * jq + 2] * s.scale, dqacc[db][4 * jq + 3] * s.scale);
+        *reinterpret_cast<uint2*>(drow + db * 32 + jq * 8) = pk;
+      }
+  }
+}
+
+template <int D>
+hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
+  AttnShape s;
+  s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
+  s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
+  MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
+  const int n_qt = (a.q_len + kBM - 1) / kBM;
+  const int n_hg = a.h_q / 4;
+  const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
+  bwd_dq_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
+      s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.lse, a.delta, m,
+      static_cast<uint16_t*>(a.dq), n_qt, n_hg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim) {
+  // a (batch row, K/V head)'s keys, including the last tile's keys past the
+  // row, must be addressable with 31-bit buffer offsets
+  return (seq_len + kBN) * h_kv * head_dim * 2 < (int64_t{1} << 31);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
+  return a.head_dim == 64 ? bwd_dq_t<64>(a, st) : bwd_dq_t<128>(a, st);
+}
+
+}  // namespace bd

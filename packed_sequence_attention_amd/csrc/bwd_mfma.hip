@@ -1,4 +1,5 @@
-// bf16 matrix-core backward of block-diagonal packed attention for gfx950.
+// bf16 matrix-core dK/dV kernel of the block-diagonal packed attention
+// backward for gfx950 (key-stationary), plus the backward's launch sequence.
 //
 // Automodel page "feat(distributed): block-diagonal varlen CP for packed
 // sequences", Proof section (forward/backward parity, input gradients) and
@@ -7,7 +8,8 @@
 //   P_ij  = exp(scale q_i.k_j - LSE_i)          (LSE saved by the forward)
 //   dP_ij = dO_i . v_j,   delta_i = dO_i . O_i  (= sum_j P_ij dP_ij)
 //   dS_ij = P_ij (dP_ij - delta_i)
-//   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j
+//   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i
+// (dQ is computed by the query-stationary kernel in bwd_dq.hip.)
 //
 // Work decomposition: a workgroup owns 128 keys (4 waves x 32) of one K/V
 // head of one batch row and sweeps the group's query heads and the 32-row
@@ -17,26 +19,18 @@
 //   S = Q K^T and dP = dO V^T   (A = Q / dO rows from LDS, B = K / V in registers)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A = dO^T / Q^T via the LDS transpose
 //                                    load, B = P / dS from the accumulators)
-// dS^T is written to LDS; then the tile's dQ (32 rows x head_dim) is computed
-// over all 128 keys (A = dS via transpose load, B = K via transpose load) and
-// added to a float32 accumulator with buffer atomics (the buffer's range
-// check drops rows past the chunk); a final kernel scales and rounds it.
 // dK and dV stay in registers until the end and are written once
 // (deterministic).  The element mask uses the per-key row interval
-// [key_qlo, key_qhi) and is applied only to blocks that are not entirely
-// allowed; waves whose keys no row of the tile attends skip the tile.
+// [key_qlo, key_qhi); it also zeroes padding rows and rows past the chunk.
 //
-// LDS layouts are chosen so every access pattern is free of bank conflicts
-// (64 banks of 4 bytes; 16-byte reads serve 16 lanes per cycle, 8-byte reads
-// and transpose loads 32 lanes):
-//   Q / dO tiles: rows of head_dim bf16 without padding; the 16-byte chunk c
-//   of row r is stored at chunk c ^ f(r), with f chosen so that 16 rows of a
-//   row read and 4 rows x 4 chunks of a transpose read all land on distinct
-//   banks.  K tile: rows padded by 64 bytes.  dS^T: 64-byte rows with the
-//   chunk index xor-ed by bits 2..3 of the row.
-// Q / dO / LSE / delta of the next query tile are loaded straight into the
-// other half of an LDS double buffer (LDS-DMA) while the current one is
-// processed.
+// LDS layout (64 banks of 4 bytes; 16-byte reads serve 16 lanes per cycle,
+// 8-byte reads and transpose loads 32 lanes): Q / dO tiles are rows of
+// head_dim bf16 without padding; the 16-byte chunk c of row r is stored at
+// chunk c ^ f(r), with f chosen so that 16 rows of a row read and 4 rows x 4
+// chunks of a transpose read all land on distinct banks.  Q / dO / LSE /
+// delta of the next query tile are loaded straight into the other half of an
+// LDS double buffer (LDS-DMA) while the current one is processed; one
+// barrier per iteration.
 #include <limits.h>
 #include <math.h>
 
@@ -51,14 +45,11 @@ constexpr int kQB = 32;   // query rows per tile
 
 template <int D>
 struct BwdLds {
-  static constexpr int KP = D * 2 + 64;  // K tile row pitch (transpose loads)
-  static constexpr int QP = D * 2;       // Q / dO tile row pitch (xor-swizzled chunks)
-  static constexpr int SP = kQB * 2;     // dS^T row pitch (32 bf16)
+  static constexpr int QP = D * 2;                  // Q / dO tile row pitch (xor-swizzled chunks)
   static constexpr int stat = 2 * kQB * 4;          // lse, delta
   static constexpr int qbuf = 2 * kQB * QP + stat;  // one Q/dO/statistics buffer
-  static constexpr int off_q = kKB * KP;            // two qbuf follow the K tile
-  static constexpr int off_ds = off_q + 2 * qbuf;
-  static constexpr int off_red = off_ds + 2 * kKB * SP;  // two dS^T buffers
+  static constexpr int off_q = 0;                   // two qbuf
+  static constexpr int off_red = off_q + 2 * qbuf;
   static constexpr int bytes = off_red + 16 * 4;
   static constexpr int NCH = kQB * (D / 8) / 256;   // 16-byte direct loads per thread per tensor
 };
@@ -78,26 +69,29 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const float* __restrict__ delta, MetaView m, float* __restrict__ dq_acc,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int n_kt) {
+    const float* __restrict__ delta, MetaView m, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int n_kt, int n_bg) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
   using L = BwdLds<D>;
   constexpr int NCH = L::NCH;
   __shared__ __attribute__((aligned(16))) char smem[L::bytes];
-  char* sK = smem;
-  char* sdS = smem + L::off_ds;
   int* sRed = reinterpret_cast<int*>(smem + L::off_red);  // 16 ints of reduction scratch
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
 
-  const int kt = static_cast<int>(blockIdx.x) % n_kt;
-  const int bg = static_cast<int>(blockIdx.x) / n_kt;
+  // Workgroups are dispatched to the 8 XCDs round-robin by index; keep every
+  // key tile of one (batch row, K/V head) on one XCD so their reads of the
+  // same Q / dO tiles can hit that XCD's L2.
+  const int xcd = static_cast<int>(blockIdx.x) & 7, slot = static_cast<int>(blockIdx.x) >> 3;
+  const int bg = xcd + 8 * (slot / n_kt);
+  const int kt = slot % n_kt;
+  if (bg >= n_bg) return;  // whole workgroup: no barrier has been reached
   const int b = bg / s.h_kv, g = bg % s.h_kv;
   const int k0 = kt * kKB;
   const int kw0 = k0 + wave * 32;
@@ -117,20 +111,6 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
       for (int i = 0; i < 8; ++i) kf[kk][i] = vf[kk][i] = static_cast<__bf16>(0.f);
     }
   }
-  // Stage the whole K tile for the dQ product.
-  for (int ci = tid; ci < kKB * CH; ci += 256) {
-    const int r = ci / CH, col = ci % CH;
-    const int j = k0 + r;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (j < s.seq_len)
-      x = *reinterpret_cast<const uint4*>(
-          k + ((static_cast<int64_t>(b) * s.seq_len + j) * s.h_kv + g) * D + col * 8);
-    *reinterpret_cast<uint4*>(sK + r * L::KP + col * 16) = x;
-  }
-  // Both dS^T buffers start at zero (the first iteration's deferred dQ
-  // product reads one of them).
-  for (int i = tid; i < 2 * kKB * L::SP / 16; i += 256)
-    reinterpret_cast<uint4*>(sdS)[i] = make_uint4(0, 0, 0, 0);
   // Local rows attending this lane's key: [qlo_k, qhi_k) (empty: qlo_k >= qhi_k).
   int qlo_k = INT_MAX, qhi_k = INT_MIN;
   if (key_ok) {
@@ -164,16 +144,7 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
   const int tr_row = 4 * kg + ((lane & 15) >> 2);   // transpose-load row within a group of 8
   const int tr_g = (lane >> 4) & 1;                 // 16-column half of a transpose load
   const int tr_s = lane & 3;                        // 4-column quarter
-  const int tr_col = (16 * tr_g + 4 * tr_s) * 2;    // byte column (unswizzled layouts)
-  // dQ split: wave -> (d block, key part).
-  constexpr int DQ_PARTS = 4 / DB;
-  constexpr int DQ_KEYS = kKB / DQ_PARTS;
-  const int dq_db = wave % DB;
-  const int dq_k0 = (wave / DB) * DQ_KEYS;
-  // dQ accumulator rows of (b, h) are addressed through a buffer whose range
-  // ends at row q_len, so rows past the chunk are dropped by the hardware.
   const int row_stride = s.h_q * D;  // elements between consecutive rows
-  const int dq_voff = ((kg * 4) * row_stride + dq_db * 32 + n) * 4;
 
   // Q / dO / statistics staging: direct global -> LDS loads (buffer form,
   // so rows past the chunk read as zero) into an LDS double buffer, issued
@@ -221,60 +192,21 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
     }
   };
 
-  // dQ of one finished tile: rows tt0..tt0+31 of head hh, d block dq_db, keys
-  // dq_k0 .. +DQ_KEYS of this workgroup, from dS^T in LDS; float32 atomics.
-  auto dq_tile = [&](const char* dsbuf, int hh, int tt0) {
-    f32x16 qacc;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) qacc[j] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < DQ_KEYS / 16; ++ks) {
-      const int ra = dq_k0 + ks * 16 + tr_row, rb = ra + 8;
-      const int chunk = 2 * tr_g + (tr_s >> 1), half = (tr_s & 1) * 8;
-      const bf16x8 a_ds = lds_tr_pair(dsbuf + ra * L::SP + ((chunk ^ ((ra >> 2) & 3)) << 4) + half,
-                                      dsbuf + rb * L::SP + ((chunk ^ ((rb >> 2) & 3)) << 4) + half);
-      const bf16x8 b_k = lds_tr_pair(sK + ra * L::KP + tr_col + dq_db * 64,
-                                     sK + rb * L::KP + tr_col + dq_db * 64);
-      qacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_ds, b_k, qacc, 0, 0, 0);
-    }
-    // qacc[j] = dQ[row tt0 + (j/4)*8 + kg*4 + j%4][d = 32*dq_db + n]
-    float* base = dq_acc + (static_cast<int64_t>(b) * s.q_len * s.h_q + hh) * D;
-    const int nbytes = (s.q_len * row_stride - hh * D) * 4;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(base, 0, nbytes, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int soff = (tt0 + (j >> 2) * 8 + (j & 3)) * row_stride * 4;
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(qacc[j], rsrc, dq_voff, soff, 0);
-    }
-  };
-
-  // Software pipeline, one barrier per iteration.  Iteration it: the dQ
-  // product of tile it-1 (its dS^T is complete in the other dS^T buffer) and
-  // its atomics; the direct loads of tile it+1 into the other Q/dO buffer;
-  // S, dP, the softmax, dS^T and the dV/dK products of tile it; then a wait
-  // for all outstanding memory operations and the barrier.  The dQ product of
-  // the last tile follows the loop.
-  const int krow = wave * 32 + n;
-  const int ksw = (krow >> 2) & 3;
+  // One barrier per iteration.  Iteration it: the direct loads of tile it+1
+  // into the other Q/dO buffer; S, dP, the softmax and the dV/dK products of
+  // tile it; then a wait for the loads and the barrier.
   if (n_it > 0) {
     issue_loads(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  int prev_h = g * s.group, prev_t0 = qt0 * kQB;
   for (int it = 0; it < n_it; ++it) {
     const int buf = it & 1;
-    const int h = g * s.group + it / n_q;
     const int t0 = (qt0 + it % n_q) * kQB;
     const char* sQ = smem + L::off_q + buf * L::qbuf;
     const char* sdO = sQ + kQB * L::QP;
     const float* sLse = reinterpret_cast<const float*>(sdO + kQB * L::QP);
     const float* sDel = sLse + kQB;
-    char* ds_cur = sdS + buf * (kKB * L::SP);
-    const char* ds_prev = sdS + (buf ^ 1) * (kKB * L::SP);
-
-    // dQ of the previous tile (for it == 0: an all-zero dS^T buffer).
-    dq_tile(ds_prev, prev_h, prev_t0);
     if (it + 1 < n_it) issue_loads(it + 1, buf ^ 1);  // that buffer was last read before the last barrier
 
     f32x16 sacc, pacc;
@@ -321,14 +253,6 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
       dsb[0][i] = static_cast<__bf16>(dsv[i]);
       dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
     }
-    // dS^T row of this lane's key: 4 consecutive query rows per store.
-#pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      uint2 pk;
-      pk.x = pack_bf16x2(dsv[4 * jq], dsv[4 * jq + 1]);
-      pk.y = pack_bf16x2(dsv[4 * jq + 2], dsv[4 * jq + 3]);
-      *reinterpret_cast<uint2*>(ds_cur + krow * L::SP + ((jq ^ ksw) << 4) + kg * 8) = pk;
-    }
     // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, accumulator order).
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
@@ -346,12 +270,9 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
         dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q, dsb[kk2], dkacc[db], 0, 0, 0);
       }
     }
-    prev_h = h;
-    prev_t0 = t0;
     __builtin_amdgcn_s_waitcnt(0);  // direct loads of tile it+1 have landed in LDS
-    __syncthreads();                // dS^T of this tile complete; next Q/dO buffer ready
+    __syncthreads();                // next Q/dO buffer ready
   }
-  if (n_it > 0) dq_tile(sdS + (n_it & 1 ? 0 : 1) * (kKB * L::SP), prev_h, prev_t0);
 
   // dK, dV of this lane's key: dvacc[db][j] = dV^T[d = 32db + (j/4)*8 + kg*4 + j%4][key n]
   if (key_ok) {
@@ -372,22 +293,6 @@ __global__ __launch_bounds__(256, 1) void bwd_mfma_kernel(
   }
 }
 
-// dQ = bf16(scale * dq_acc), 8 elements per thread.
-__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
-                                                          uint16_t* __restrict__ dq, int64_t n8,
-                                                          float scale) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= n8) return;
-  const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
-  const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
-  uint4 r;
-  r.x = pack_bf16x2(a.x * scale, a.y * scale);
-  r.y = pack_bf16x2(a.z * scale, a.w * scale);
-  r.z = pack_bf16x2(b.x * scale, b.y * scale);
-  r.w = pack_bf16x2(b.z * scale, b.w * scale);
-  reinterpret_cast<uint4*>(dq)[i] = r;
-}
-
 template <int D>
 hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
   AttnShape s;
@@ -397,34 +302,29 @@ hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
   hipError_t e = launch_bwd_prep(a, st);
   if (e != hipSuccess) return e;
   const int n_kt = (a.seq_len + kKB - 1) / kKB;
-  const int64_t grid = static_cast<int64_t>(n_kt) * a.batch * a.h_kv;
-  if (grid > 0) {
+  const int n_bg = a.batch * a.h_kv;
+  const int64_t grid = 8 * static_cast<int64_t>((n_bg + 7) / 8) * n_kt;
+  if (n_kt > 0) {
     e = mark(a.mark_start, st);
     if (e != hipSuccess) return e;
-    bwd_mfma_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
+    bwd_dkdv_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
         s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.lse, a.delta, m,
-        a.dq_acc, static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt);
+        static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = mark(a.mark_stop, st);
     if (e != hipSuccess) return e;
   }
-  const int64_t n8 = static_cast<int64_t>(a.batch) * a.q_len * a.h_q * D / 8;
-  if (n8 > 0) {
-    dq_finalize_kernel<<<dim3(static_cast<unsigned>((n8 + 255) / 256)), 256, 0, st>>>(
-        a.dq_acc, static_cast<uint16_t*>(a.dq), n8, a.scale);
-    e = hipGetLastError();
-  }
-  return e;
+  return launch_bwd_dq(a, st);
 }
 
 }  // namespace
 
 bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim) {
-  // a (batch row, head)'s dQ accumulator window must be addressable with
-  // 32-bit buffer offsets
-  return q_len * h_q * head_dim * 4 < (int64_t{1} << 31);
+  // a (batch row, head)'s Q / dO rows, including the last tile's rows past
+  // the chunk, must be addressable with 31-bit buffer offsets
+  return (q_len + kQB) * h_q * head_dim * 2 < (int64_t{1} << 31);
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {

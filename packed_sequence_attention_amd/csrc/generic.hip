@@ -263,15 +263,13 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
   }
 }
 
-// delta = sum_d dO * O in float32 for every (b, local row, query head), and
-// (when given) zero that row of the float32 dQ accumulator.  A group of lpr
+// delta = sum_d dO * O in float32 for every (b, local row, query head).  A group of lpr
 // lanes (a power of two >= head_dim / 8) handles one row with 16-byte
 // accesses, so consecutive lanes touch consecutive memory.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnShape s, const T* __restrict__ o,
                                                        const T* __restrict__ d_o,
-                                                       float* __restrict__ delta,
-                                                       float* __restrict__ dq_acc, int lpr) {
+                                                       float* __restrict__ delta, int lpr) {
   const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t idx = gtid / lpr;  // row (b, t, h), h fastest
   const int sub = static_cast<int>(gtid % lpr);
@@ -285,11 +283,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnShape s, const T* __r
     load8(d_o + idx * D + sub * 8, y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
-    if (dq_acc != nullptr) {
-      float4* z = reinterpret_cast<float4*>(dq_acc + idx * D + sub * 8);
-      z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
   }
   for (int off = lpr >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (sub == 0 && idx < total) {
@@ -339,7 +332,7 @@ hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
   const int lpr = lanes_per_row(a.head_dim);
   bwd_prep_kernel<T><<<static_cast<unsigned>((rows * lpr + 255) / 256), 256, 0, st>>>(
-      s, static_cast<const T*>(a.o), static_cast<const T*>(a.d_o), a.delta, nullptr, lpr);
+      s, static_cast<const T*>(a.o), static_cast<const T*>(a.d_o), a.delta, lpr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dq_generic_kernel<T, NR><<<blocks_for(rows), 256, 0, st>>>(
@@ -400,10 +393,10 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
   const unsigned grid = static_cast<unsigned>((rows * lpr + 255) / 256);
   if (a.dtype == 0)
     bwd_prep_kernel<float><<<grid, 256, 0, st>>>(s, static_cast<const float*>(a.o),
-                                                 static_cast<const float*>(a.d_o), a.delta, a.dq_acc, lpr);
+                                                 static_cast<const float*>(a.d_o), a.delta, lpr);
   else
     bwd_prep_kernel<uint16_t><<<grid, 256, 0, st>>>(s, static_cast<const uint16_t*>(a.o),
-                                                    static_cast<const uint16_t*>(a.d_o), a.delta, a.dq_acc, lpr);
+                                                    static_cast<const uint16_t*>(a.d_o), a.delta, lpr);
   return hipGetLastError();
 }
 

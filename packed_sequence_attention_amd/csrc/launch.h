@@ -38,7 +38,6 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;   // workspace: [batch][h_q][q_len]
-  float* dq_acc;  // workspace: [batch][q_len][h_q][head_dim] (matrix-core path only)
   hipEvent_t mark_start;  // recorded around the main kernel when non-null
   hipEvent_t mark_stop;
 };
@@ -55,12 +54,14 @@ hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t stream);
 bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
-// The matrix-core backward addresses one (batch row, head)'s float32 dQ
-// accumulator rows with 32-bit buffer offsets.
+// The matrix-core backward addresses one (batch row, head)'s Q / dO rows and
+// one (batch row, K/V head)'s keys with 32-bit buffer offsets.
 bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim);
+bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim);
+// dQ of the matrix-core backward (query-stationary; needs delta).
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
-// Backward row statistics: delta = rowsum(dO * O) in float32, and (if
-// dq_acc is non-null) zero the float32 dQ accumulator.
+// Backward row statistics: delta = rowsum(dO * O) in float32.
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
 
 // Fill n 16-bit words with zeros (a kernel, so it is safe under graph capture).
