@@ -11,26 +11,32 @@
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i
 // (dQ is computed by the query-stationary kernel in bwd_dq.hip.)
 //
-// Work decomposition: a workgroup owns 128 keys (4 waves x 32) of one K/V
-// head of one batch row and sweeps the group's query heads and the 32-row
-// query tiles that attend any of its keys ([min key_qlo, max key_qhi) from
-// the per-step metadata).  Per query tile each wave computes, for its 32
-// keys (v_mfma_f32_32x32x16_bf16, lane l: key l % 32):
+// Work decomposition: a workgroup owns 64 keys of one K/V head of one batch
+// row and runs 8 waves: two key groups of 32 times four query heads of the
+// GQA group, so the heads are processed concurrently rather than one after
+// another (the key tiles at the start of a long document attend many query
+// tiles; splitting their work by head shortens the longest workgroup 4x).
+// Each wave sweeps the 32-row query tiles that attend any of the
+// workgroup's keys ([min key_qlo, max key_qhi) from the per-step metadata),
+// once per group of four heads, and computes for its 32 keys
+// (v_mfma_f32_32x32x16_bf16, lane l: key l % 32):
 //   S = Q K^T and dP = dO V^T   (A = Q / dO rows from LDS, B = K / V in registers)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A = dO^T / Q^T via the LDS transpose
 //                                    load, B = P / dS from the accumulators)
-// dK and dV stay in registers until the end and are written once
-// (deterministic).  The element mask uses the per-key row interval
-// [key_qlo, key_qhi); it also zeroes padding rows and rows past the chunk.
+// dK and dV stay in registers until the end; the four heads' partial sums
+// of each key are then added through LDS in a fixed order ((h0 + h2) +
+// (h1 + h3)) and written once (deterministic).  The element mask uses the
+// per-key row interval [key_qlo, key_qhi); it also zeroes padding rows and
+// rows past the chunk.
 //
 // LDS layout (64 banks of 4 bytes; 16-byte reads serve 16 lanes per cycle,
 // 8-byte reads and transpose loads 32 lanes): Q / dO tiles are rows of
 // head_dim bf16 without padding; the 16-byte chunk c of row r is stored at
 // chunk c ^ f(r), with f chosen so that 16 rows of a row read and 4 rows x 4
 // chunks of a transpose read all land on distinct banks.  Q / dO / LSE /
-// delta of the next query tile are loaded straight into the other half of an
-// LDS double buffer (LDS-DMA) while the current one is processed; one
-// barrier per iteration.
+// delta of the next query tile of each head are loaded straight into the
+// other half of an LDS double buffer (LDS-DMA) while the current one is
+// processed; one barrier per iteration.
 #include <limits.h>
 #include <math.h>
 
@@ -40,18 +46,23 @@
 namespace bd {
 namespace {
 
-constexpr int kKB = 128;  // keys per workgroup
-constexpr int kQB = 32;   // query rows per tile
+constexpr int kKW = 32;        // keys per wave
+constexpr int kKB = 2 * kKW;   // keys per workgroup
+constexpr int kQB = 32;        // query rows per tile
+constexpr int kHW = 4;         // query heads processed concurrently
 
 template <int D>
 struct BwdLds {
   static constexpr int QP = D * 2;                  // Q / dO tile row pitch (xor-swizzled chunks)
   static constexpr int stat = 2 * kQB * 4;          // lse, delta
-  static constexpr int qbuf = 2 * kQB * QP + stat;  // one Q/dO/statistics buffer
-  static constexpr int off_q = 0;                   // two qbuf
-  static constexpr int off_red = off_q + 2 * qbuf;
+  static constexpr int head = 2 * kQB * QP + stat;  // one head's Q, dO, statistics (one stage)
+  static constexpr int off_v = kHW * 2 * head;      // [head][stage] tiles, then the V tile
+  static constexpr int off_red = off_v + kKB * QP;  // then reduction scratch
   static constexpr int bytes = off_red + 16 * 4;
-  static constexpr int NCH = kQB * (D / 8) / 256;   // 16-byte direct loads per thread per tensor
+  static constexpr int NCH = kQB * (D / 8) / 64;    // 16-byte direct loads per wave per tensor
+  static constexpr int part = kKW * D * 2 * 4;      // one wave's dK and dV partials (float32)
+  static_assert(4 * part <= off_v, "head reduction must fit in the tile buffers");
+  static_assert(head + 2 * kQB * QP + stat <= 65535, "stage offsets must fit LDS immediate offsets");
 };
 
 // Chunk swizzle of row r of a Q / dO tile (see the file comment).
@@ -61,6 +72,11 @@ __device__ __forceinline__ int qswz(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+template <int B>
+struct Stage {
+  static constexpr int value = B;
+};
+
 __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
@@ -69,7 +85,7 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const float* __restrict__ delta, MetaView m, uint16_t* __restrict__ dk,
@@ -82,7 +98,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) char smem[L::bytes];
   int* sRed = reinterpret_cast<int*>(smem + L::off_red);  // 16 ints of reduction scratch
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kgrp = wave & 1, hsub = wave >> 1;  // key group, head within the four
   const int n = lane & 31, kg = lane >> 5;
 
   // Workgroups are dispatched to the 8 XCDs round-robin by index; keep every
@@ -93,22 +111,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int kt = slot % n_kt;
   if (bg >= n_bg) return;  // whole workgroup: no barrier has been reached
   const int b = bg / s.h_kv, g = bg % s.h_kv;
-  const int k0 = kt * kKB;
-  const int kw0 = k0 + wave * 32;
-  const int key = kw0 + n;  // this lane's key (columns of S)
+  const int key = kt * kKB + kgrp * kKW + n;  // this lane's key (columns of S)
   const bool key_ok = key < s.seq_len;
   const int64_t kv_row = (static_cast<int64_t>(b) * s.seq_len + key) * s.h_kv + g;
 
-  // K / V fragments of this wave's keys (B operands of S and dP).
-  bf16x8 kf[KK], vf[KK];
+  // K fragments of this wave's keys (B operand of S) in registers; the
+  // workgroup's V tile (B operand of dP) in LDS, swizzled like Q / dO.
+  bf16x8 kf[KK];
+  char* sV = smem + L::off_v + kgrp * kKW * L::QP;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (key_ok) {
       kf[kk] = *reinterpret_cast<const bf16x8*>(k + kv_row * D + kk * 16 + kg * 8);
-      vf[kk] = *reinterpret_cast<const bf16x8*>(v + kv_row * D + kk * 16 + kg * 8);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kf[kk][i] = vf[kk][i] = static_cast<__bf16>(0.f);
+      for (int i = 0; i < 8; ++i) kf[kk][i] = static_cast<__bf16>(0.f);
+    }
+  }
+  if (hsub == 0) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 x;
+      if (key_ok) {
+        x = *reinterpret_cast<const bf16x8*>(v + kv_row * D + kk * 16 + kg * 8);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = static_cast<__bf16>(0.f);
+      }
+      *reinterpret_cast<bf16x8*>(sV + n * L::QP + (((2 * kk + kg) ^ qswz<D>(n)) << 4)) = x;
     }
   }
   // Local rows attending this lane's key: [qlo_k, qhi_k) (empty: qlo_k >= qhi_k).
@@ -125,13 +155,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // Element mask: row t is allowed iff (unsigned)(t - mask_lo) < mask_span.
   const int mask_lo = qhi_k > qlo_k ? qlo_k : 0;
   const unsigned mask_span = qhi_k > qlo_k ? static_cast<unsigned>(qhi_k - qlo_k) : 0u;
-  if (lane == 0) {
-    sRed[wave] = wqlo;
-    sRed[4 + wave] = wqhi;
+  if (lane == 0 && hsub == 0) {
+    sRed[kgrp] = wqlo;
+    sRed[2 + kgrp] = wqhi;
   }
   __syncthreads();
-  const int gqlo = min(min(sRed[0], sRed[1]), min(sRed[2], sRed[3]));
-  const int gqhi = max(max(sRed[4], sRed[5]), max(sRed[6], sRed[7]));
+  const int gqlo = min(sRed[0], sRed[1]);
+  const int gqhi = max(sRed[2], sRed[3]);
 
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -148,37 +178,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   // Q / dO / statistics staging: direct global -> LDS loads (buffer form,
   // so rows past the chunk read as zero) into an LDS double buffer, issued
-  // one iteration ahead.  Iteration it covers query head g*group + it / n_q
-  // and the query tile qt0 + it % n_q.  Q / dO land in the swizzled layout:
-  // lane l of a load writes LDS chunk (base + l), so each lane fetches the
-  // global chunk that belongs at that position.
+  // one iteration ahead.  Iteration it covers the query tile qt0 + it % n_q
+  // of head g*group + (it / n_q)*4 + hsub for the wave pair hsub; of that
+  // pair, key group 0 loads Q and the statistics, key group 1 loads dO.
+  // Q / dO land in the swizzled layout: lane l of a load writes LDS chunk
+  // (base + l), so each lane fetches the global chunk that belongs there.
   const int qt0 = gqlo / kQB;
   const int n_q = gqhi > gqlo ? (gqhi - 1) / kQB - qt0 + 1 : 0;
-  const int n_it = n_q * s.group;
+  const int n_it = n_q * (s.group / kHW);
   typedef __attribute__((address_space(3))) void lds_void;
   auto issue_loads = [&](int it, int buf) {
-    const int h = g * s.group + it / n_q;
+    const int h = g * s.group + (it / n_q) * kHW + hsub;
     const int t0 = (qt0 + it % n_q) * kQB;
     const int64_t head0 = (static_cast<int64_t>(b) * s.q_len * s.h_q + h) * D;  // row 0 of (b, h)
     const int nbytes = (s.q_len * row_stride - h * D) * 2;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(q + head0), 0, nbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(d_o + head0), 0, nbytes, 0x00020000);
-    char* sQb = smem + L::off_q + buf * L::qbuf;
-    char* sdOb = sQb + kQB * L::QP;
+    const uint16_t* src = kgrp == 0 ? q : d_o;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src + head0), 0, nbytes, 0x00020000);
+    char* hb = smem + (hsub * 2 + buf) * L::head;
+    char* dst = hb + kgrp * (kQB * L::QP);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int lc = i * 256 + tid;  // LDS chunk written by this lane
+      const int lc = i * 64 + lane;  // LDS chunk written by this lane
       const int r = lc / CH, pchunk = lc % CH;
-      const int c = pchunk ^ qswz<D>(r);
-      const int voff = ((t0 + r) * row_stride + c * 8) * 2;
-      const int lbase = (i * 256 + wave * 64) * 16;  // wave-uniform LDS destination
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)(sQb + lbase), 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void*)(sdOb + lbase), 16, voff, 0, 0, 0);
+      const int cc = pchunk ^ qswz<D>(r);
+      const int voff = ((t0 + r) * row_stride + cc * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 64 * 16), 16, voff, 0, 0, 0);
     }
-    if (wave == 0) {  // LSE to stat[0..31], delta to stat[32..63]
-      char* stat = sdOb + kQB * L::QP;
+    if (kgrp == 0) {  // LSE to stat[0..31], delta to stat[32..63]
+      char* stat = hb + 2 * kQB * L::QP;
       const int64_t st0 = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len;
       const int sbytes = s.q_len * 4;
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
@@ -200,10 +228,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  for (int it = 0; it < n_it; ++it) {
-    const int buf = it & 1;
+  // The loop is unrolled by two so that the stage is a compile-time
+  // constant and every LDS address is a per-lane base plus an immediate.
+  const char* hbase = smem + hsub * 2 * L::head;
+  auto step = [&](int it, auto stage) {
+    constexpr int buf = decltype(stage)::value;
     const int t0 = (qt0 + it % n_q) * kQB;
-    const char* sQ = smem + L::off_q + buf * L::qbuf;
+    const char* sQ = hbase + buf * L::head;
     const char* sdO = sQ + kQB * L::QP;
     const float* sLse = reinterpret_cast<const float*>(sdO + kQB * L::QP);
     const float* sDel = sLse + kQB;
@@ -220,8 +251,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         const int pos = nat_row + (((2 * kk + kg) ^ nat_swz) << 4);
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + pos);
         const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sdO + pos);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sV + pos);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], pacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, pacc, 0, 0, 0);
       }
     }
     // sacc[j] = S[row t0 + (j/4)*8 + kg*4 + j%4][key n].  P is zero outside
@@ -272,7 +304,54 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     __builtin_amdgcn_s_waitcnt(0);  // direct loads of tile it+1 have landed in LDS
     __syncthreads();                // next Q/dO buffer ready
+  };
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, Stage<0>{});
+    if (it + 1 < n_it) step(it + 1, Stage<1>{});
   }
+
+  // Sum the four heads' partials in a fixed order, (h0 + h2) + (h1 + h3),
+  // through LDS (the tile buffers are free once every wave has left the
+  // loop).  A wave's partial is stored lane-major, one float4 per lane per
+  // step, so stores and loads are contiguous.
+  __syncthreads();
+  float4* red = reinterpret_cast<float4*>(smem);
+  constexpr int P4 = L::part / 16;  // float4 per wave partial
+  auto put = [&](int slot_) {
+    float4* p = red + slot_ * P4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int f = (db * 4 + jq) * 2;
+        p[f * 64 + lane] = make_float4(dkacc[db][4 * jq], dkacc[db][4 * jq + 1], dkacc[db][4 * jq + 2],
+                                       dkacc[db][4 * jq + 3]);
+        p[(f + 1) * 64 + lane] = make_float4(dvacc[db][4 * jq], dvacc[db][4 * jq + 1],
+                                             dvacc[db][4 * jq + 2], dvacc[db][4 * jq + 3]);
+      }
+  };
+  auto add = [&](int slot_) {
+    const float4* p = red + slot_ * P4;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int f = (db * 4 + jq) * 2;
+        const float4 x = p[f * 64 + lane], y = p[(f + 1) * 64 + lane];
+        dkacc[db][4 * jq] += x.x; dkacc[db][4 * jq + 1] += x.y;
+        dkacc[db][4 * jq + 2] += x.z; dkacc[db][4 * jq + 3] += x.w;
+        dvacc[db][4 * jq] += y.x; dvacc[db][4 * jq + 1] += y.y;
+        dvacc[db][4 * jq + 2] += y.z; dvacc[db][4 * jq + 3] += y.w;
+      }
+  };
+  if (hsub >= 2) put((hsub - 2) * 2 + kgrp);
+  __syncthreads();
+  if (hsub < 2) add(hsub * 2 + kgrp);
+  __syncthreads();
+  if (hsub == 1) put(kgrp);
+  __syncthreads();
+  if (hsub != 0) return;
+  add(kgrp);
 
   // dK, dV of this lane's key: dvacc[db][j] = dV^T[d = 32db + (j/4)*8 + kg*4 + j%4][key n]
   if (key_ok) {
@@ -307,7 +386,7 @@ hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
   if (n_kt > 0) {
     e = mark(a.mark_start, st);
     if (e != hipSuccess) return e;
-    bwd_dkdv_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
+    bwd_dkdv_kernel<D><<<dim3(static_cast<unsigned>(grid)), 512, 0, st>>>(
         s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
         static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.lse, a.delta, m,
         static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg);
