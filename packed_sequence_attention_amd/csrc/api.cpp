@@ -101,7 +101,7 @@ extern "C" size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t 
   (void)dtype; (void)seq_len; (void)h_kv;
   if (!is_bwd || batch <= 0 || q_len <= 0 || h_q <= 0 || head_dim <= 0) return 0;
   const size_t rows = static_cast<size_t>(batch) * q_len * h_q;
-  return align256(rows * sizeof(float));  // delta
+  return align256(rows * 2 * sizeof(float));  // rowstat pairs
 }
 
 extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,

@@ -38,8 +38,7 @@ constexpr int kBM = 32;  // query rows per workgroup
 template <int D>
 struct DqLds {
   static constexpr int RP = D * 2;                  // row pitch (bytes), swizzled chunks
-  static constexpr int tile = 2 * kBN * RP;         // K tile then V tile
-  static constexpr int bytes = 2 * tile;            // double buffered
+  static constexpr int tile = 2 * kBN * RP;         // K tile then V tile (one stage)
   static constexpr int NCH = kBN * (D / 8) / 256;   // direct loads per thread per tensor
 };
 
@@ -48,6 +47,11 @@ __device__ __forceinline__ int rswz(int r) {
   if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
+
+template <int B>
+struct Stage {
+  static constexpr int value = B;
+};
 
 __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
@@ -59,14 +63,18 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const float* __restrict__ delta, MetaView m, uint16_t* __restrict__ dq, int n_qt, int n_hg) {
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dq, int n_qt, int n_hg) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
   using L = DqLds<D>;
   constexpr int RP = L::RP;
-  __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+  // The two stages are separate LDS objects: the compiler then knows that
+  // the direct loads into one stage do not alias reads of the other, and
+  // does not make those reads wait for the loads in flight.
+  __shared__ __attribute__((aligned(16))) char stage0[L::tile];
+  __shared__ __attribute__((aligned(16))) char stage1[L::tile];
   typedef __attribute__((address_space(3))) void lds_void;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -89,8 +97,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     lo = m.row_lo[bt];
     hi = m.row_hi[bt];
     const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
-    lse2 = lse[st] * kLog2e;  // -inf on padding rows: masked below
-    dlt = delta[st];
+    const float2 rs = *reinterpret_cast<const float2*>(rowstat + 2 * st);
+    lse2 = rs.x;  // lse * log2(e); -inf on padding rows: masked below
+    dlt = rs.y;
   }
   const bool real = hi > lo;
   const int kmin = wave_min_i(real ? lo : INT_MAX);
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + kv0), 0, kv_bytes, 0x00020000);
   auto issue_tile = [&](int kt, int buf) {
-    char* sK = smem + buf * L::tile;
+    char* sK = buf == 0 ? stage0 : stage1;
     char* sV = sK + kBN * RP;
 #pragma unroll
     for (int i = 0; i < L::NCH; ++i) {
@@ -153,10 +162,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     issue_tile(kt0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = kt0; kt <= kt1; ++kt) {
-      const int buf = (kt - kt0) & 1;
+    // Unrolled by two so that the stage is a compile-time constant.
+    auto step = [&](int kt, auto stage) {
+      constexpr int buf = decltype(stage)::value;
       if (kt < kt1) issue_tile(kt + 1, buf ^ 1);  // that buffer was last read before the last barrier
-      const char* sK = smem + buf * L::tile;
+      const char* sK = buf == 0 ? stage0 : stage1;
       const char* sV = sK + kBN * RP;
       const int k0 = kt * kBN;
       const bool full = all_real && lomax <= k0 && k0 + kBN - 1 <= pfirst;
@@ -208,6 +218,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       }
       __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
       __syncthreads();
+    };
+    for (int kt = kt0; kt <= kt1; kt += 2) {
+      step(kt, Stage<0>{});
+      if (kt + 1 <= kt1) step(kt + 1, Stage<1>{});
     }
   }
 
@@ -237,7 +251,7 @@ hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
   const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
   bwd_dq_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.lse, a.delta, m,
+      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.rowstat, m,
       static_cast<uint16_t*>(a.dq), n_qt, n_hg);
   return hipGetLastError();
 }

@@ -54,15 +54,13 @@ constexpr int kHW = 4;         // query heads processed concurrently
 template <int D>
 struct BwdLds {
   static constexpr int QP = D * 2;                  // Q / dO tile row pitch (xor-swizzled chunks)
-  static constexpr int stat = 2 * kQB * 4;          // lse, delta
-  static constexpr int head = 2 * kQB * QP + stat;  // one head's Q, dO, statistics (one stage)
-  static constexpr int off_v = kHW * 2 * head;      // [head][stage] tiles, then the V tile
-  static constexpr int off_red = off_v + kKB * QP;  // then reduction scratch
-  static constexpr int bytes = off_red + 16 * 4;
+  static constexpr int stat = 2 * kQB * 4;          // (lse * log2(e), delta) per row
+  static constexpr int head = 2 * kQB * QP + stat;  // one head's Q, dO, statistics
+  static constexpr int stage = kHW * head;          // one stage of the double buffer
+  static constexpr int vtile = kKB * QP;            // the workgroup's V rows
   static constexpr int NCH = kQB * (D / 8) / 64;    // 16-byte direct loads per wave per tensor
   static constexpr int part = kKW * D * 2 * 4;      // one wave's dK and dV partials (float32)
-  static_assert(4 * part <= off_v, "head reduction must fit in the tile buffers");
-  static_assert(head + 2 * kQB * QP + stat <= 65535, "stage offsets must fit LDS immediate offsets");
+  static_assert(2 * part <= stage, "head reduction must fit in the tile buffers");
 };
 
 // Chunk swizzle of row r of a Q / dO tile (see the file comment).
@@ -87,16 +85,21 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 template <int D>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const float* __restrict__ delta, MetaView m, uint16_t* __restrict__ dk,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
+    const float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int n_kt, int n_bg) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
   using L = BwdLds<D>;
   constexpr int NCH = L::NCH;
-  __shared__ __attribute__((aligned(16))) char smem[L::bytes];
-  int* sRed = reinterpret_cast<int*>(smem + L::off_red);  // 16 ints of reduction scratch
+  // The two stages are separate LDS objects: the compiler then knows that
+  // the direct loads into one stage do not alias reads of the other, and
+  // does not make those reads wait for the loads in flight.
+  __shared__ __attribute__((aligned(16))) char stage0[L::stage];
+  __shared__ __attribute__((aligned(16))) char stage1[L::stage];
+  __shared__ __attribute__((aligned(16))) char vt[L::vtile];
+  __shared__ int sRed[16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // K fragments of this wave's keys (B operand of S) in registers; the
   // workgroup's V tile (B operand of dP) in LDS, swizzled like Q / dO.
   bf16x8 kf[KK];
-  char* sV = smem + L::off_v + kgrp * kKW * L::QP;
+  char* sV = vt + kgrp * kKW * L::QP;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (key_ok) {
@@ -152,6 +155,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     }
   }
   const int wqlo = wave_min_i(qlo_k), wqhi = wave_max_i(qhi_k);
+  // Rows inside every key's interval of this wave: [kq_lo_max, kq_hi_min).
+  const int kq_lo_max = wave_max_i(qlo_k), kq_hi_min = wave_min_i(qhi_k);
   // Element mask: row t is allowed iff (unsigned)(t - mask_lo) < mask_span.
   const int mask_lo = qhi_k > qlo_k ? qlo_k : 0;
   const unsigned mask_span = qhi_k > qlo_k ? static_cast<unsigned>(qhi_k - qlo_k) : 0u;
@@ -180,64 +185,83 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // so rows past the chunk read as zero) into an LDS double buffer, issued
   // one iteration ahead.  Iteration it covers the query tile qt0 + it % n_q
   // of head g*group + (it / n_q)*4 + hsub for the wave pair hsub; of that
-  // pair, key group 0 loads Q and the statistics, key group 1 loads dO.
+  // pair, key group 0 loads Q, key group 1 loads dO and the row statistics.
   // Q / dO land in the swizzled layout: lane l of a load writes LDS chunk
   // (base + l), so each lane fetches the global chunk that belongs there.
   const int qt0 = gqlo / kQB;
   const int n_q = gqhi > gqlo ? (gqhi - 1) / kQB - qt0 + 1 : 0;
   const int n_it = n_q * (s.group / kHW);
   typedef __attribute__((address_space(3))) void lds_void;
+  // Per-lane part of the direct-load offsets: load i of a wave covers RPL
+  // tile rows (64 lanes x 16 bytes = 4 rows of 16 chunks for head_dim 128,
+  // 8 rows of 8 for 64).  The swizzle of row r depends on r % 16 only, so
+  // the lane's offset repeats every PER loads plus 16 rows; the row part
+  // common to the wave goes into the resource base.
+  constexpr int RPL = 64 / CH;  // rows per direct load
+  constexpr int PER = 16 / RPL;
   auto issue_loads = [&](int it, int buf) {
     const int h = g * s.group + (it / n_q) * kHW + hsub;
     const int t0 = (qt0 + it % n_q) * kQB;
-    const int64_t head0 = (static_cast<int64_t>(b) * s.q_len * s.h_q + h) * D;  // row 0 of (b, h)
-    const int nbytes = (s.q_len * row_stride - h * D) * 2;
+    // row t0 of (b, h); bytes from there to the end of the tensor's rows for this head
+    const int64_t tile0 = ((static_cast<int64_t>(b) * s.q_len + t0) * s.h_q + h) * D;
+    const int nbytes = ((s.q_len - t0) * row_stride - h * D) * 2;
     const uint16_t* src = kgrp == 0 ? q : d_o;
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src + head0), 0, nbytes, 0x00020000);
-    char* hb = smem + (hsub * 2 + buf) * L::head;
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src + tile0), 0, nbytes, 0x00020000);
+    char* hb = (buf == 0 ? stage0 : stage1) + hsub * L::head;
     char* dst = hb + kgrp * (kQB * L::QP);
+    // Recomputed here rather than kept live across the loop: the opaque copy
+    // of the lane index stops the compiler from hoisting (and then spilling)
+    // these offsets, whose reload would wait on the direct loads in flight.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int lane_off[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int r = i * RPL + ln / CH;  // tile row of load i (mod 16 rows)
+      lane_off[i] = (r * row_stride + ((ln % CH) ^ qswz<D>(r)) * 8) * 2;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int lc = i * 64 + lane;  // LDS chunk written by this lane
-      const int r = lc / CH, pchunk = lc % CH;
-      const int cc = pchunk ^ qswz<D>(r);
-      const int voff = ((t0 + r) * row_stride + cc * 8) * 2;
+      const int voff = lane_off[i % PER] + (i / PER) * 16 * row_stride * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 64 * 16), 16, voff, 0, 0, 0);
     }
-    if (kgrp == 0) {  // LSE to stat[0..31], delta to stat[32..63]
-      char* stat = hb + 2 * kQB * L::QP;
-      const int64_t st0 = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len;
-      const int sbytes = s.q_len * 4;
-      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(lse + st0), 0, sbytes, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(delta + st0), 0, sbytes, 0x00020000);
-      if (lane < kQB)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)stat, 4, (t0 + lane) * 4, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void*)stat, 4, (t0 + lane - kQB) * 4, 0, 0, 0);
+    if (kgrp == 1) {  // the tile's (lse * log2(e), delta) pairs: 64 x 4 bytes
+      const int64_t st0 = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t0;
+      const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(rowstat + 2 * st0), 0, (s.q_len - t0) * 8, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rst, (lds_void*)(hb + 2 * kQB * L::QP), 4, lane * 4, 0, 0, 0);
     }
   };
 
-  // One barrier per iteration.  Iteration it: the direct loads of tile it+1
-  // into the other Q/dO buffer; S, dP, the softmax and the dV/dK products of
-  // tile it; then a wait for the loads and the barrier.
+  // Two barriers per iteration, and the two wave groups run half an
+  // iteration apart ("ping-pong"): group A (heads 0, 1 of the four) and
+  // group B (heads 2, 3) each put one wave on every SIMD, and while one
+  // group runs the softmax (vector ALU) the other keeps the matrix cores
+  // busy with S and dP.  Per wave, iteration it is
+  //   H1: direct loads of tile it+1 into the other stage; S and dP products
+  //   (barrier: scheduling only, no memory ordering)
+  //   H2: softmax, dV/dK products of tile it; wait for the direct loads;
+  //   barrier.
+  // Group B enters the loop one barrier later and group A leaves it one
+  // barrier later, so every wave executes the same number of barriers.  The
+  // two groups share no tile buffers, so only the full barrier at the end of
+  // a wave's own H2 orders its group's loads and reads.
+  const bool late = hsub >= 2;
   if (n_it > 0) {
     issue_loads(0, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (late) __builtin_amdgcn_s_barrier();
   }
   // The loop is unrolled by two so that the stage is a compile-time
   // constant and every LDS address is a per-lane base plus an immediate.
-  const char* hbase = smem + hsub * 2 * L::head;
   auto step = [&](int it, auto stage) {
     constexpr int buf = decltype(stage)::value;
     const int t0 = (qt0 + it % n_q) * kQB;
-    const char* sQ = hbase + buf * L::head;
+    const char* sQ = (buf == 0 ? stage0 : stage1) + hsub * L::head;
     const char* sdO = sQ + kQB * L::QP;
-    const float* sLse = reinterpret_cast<const float*>(sdO + kQB * L::QP);
-    const float* sDel = sLse + kQB;
+    const float* sStat = reinterpret_cast<const float*>(sdO + kQB * L::QP);  // (lse2, delta) pairs
     if (it + 1 < n_it) issue_loads(it + 1, buf ^ 1);  // that buffer was last read before the last barrier
 
     f32x16 sacc, pacc;
@@ -256,52 +280,65 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, pacc, 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_barrier();  // H1 / H2 boundary (see above)
     // sacc[j] = S[row t0 + (j/4)*8 + kg*4 + j%4][key n].  P is zero outside
     // the mask, which also covers padding rows, rows past the chunk and
-    // waves whose keys no row of this tile attends.
-    float pv[16], dsv[16];
+    // waves whose keys no row of this tile attends.  Tiles inside every
+    // key's row interval skip the mask.
+    // The softmax and the dV/dK products, with or without the mask (one
+    // copy each so that nothing but the accumulators is live across the
+    // branch).
+    auto finish = [&](auto masked) {
+      float pv[16], dsv[16];
 #pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      const int r0 = jq * 8 + kg * 4;
-      const float4 ls4 = *reinterpret_cast<const float4*>(sLse + r0);
-      const float4 de4 = *reinterpret_cast<const float4*>(sDel + r0);
-      const float lsv[4] = {ls4.x * kLog2e, ls4.y * kLog2e, ls4.z * kLog2e, ls4.w * kLog2e};
-      const float dev[4] = {de4.x, de4.y, de4.z, de4.w};
+      for (int jq = 0; jq < 4; ++jq) {
+        const int r0 = jq * 8 + kg * 4;
+        const f32x4 st01 = *reinterpret_cast<const f32x4*>(sStat + 2 * r0);
+        const f32x4 st23 = *reinterpret_cast<const f32x4*>(sStat + 2 * r0 + 4);
+        const float lsv[4] = {st01[0], st01[2], st23[0], st23[2]};
+        const float dev[4] = {st01[1], st01[3], st23[1], st23[3]};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = jq * 4 + e;
-        const unsigned rel = static_cast<unsigned>(t0 + r0 + e - mask_lo);
-        float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
-        p = rel < mask_span ? p : 0.f;  // a select: also clears inf on padding rows
-        pv[j] = p;
-        dsv[j] = p * (pacc[j] - dev[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int j = jq * 4 + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
+          if constexpr (decltype(masked)::value) {
+            const unsigned rel = static_cast<unsigned>(t0 + r0 + e - mask_lo);
+            p = rel < mask_span ? p : 0.f;  // a select: also clears inf on padding rows
+          }
+          pv[j] = p;
+          dsv[j] = p * (pacc[j] - dev[e]);
+        }
       }
-    }
-    bf16x8 pb[2], dsb[2];
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pb[0][i] = static_cast<__bf16>(pv[i]);
-      pb[1][i] = static_cast<__bf16>(pv[8 + i]);
-      dsb[0][i] = static_cast<__bf16>(dsv[i]);
-      dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, accumulator order).
-#pragma unroll
-    for (int kk2 = 0; kk2 < 2; ++kk2) {
-      const int r_a = 16 * kk2 + tr_row, r_b = r_a + 8;
-      const int sw_a = qswz<D>(r_a), sw_b = qswz<D>(r_b);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
-        const int half = (tr_s & 1) * 8;
-        const int pa = r_a * L::QP + ((chunk ^ sw_a) << 4) + half;
-        const int pb_ = r_b * L::QP + ((chunk ^ sw_b) << 4) + half;
-        const bf16x8 a_do = lds_tr_pair(sdO + pa, sdO + pb_);
-        const bf16x8 a_q = lds_tr_pair(sQ + pa, sQ + pb_);
-        dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_do, pb[kk2], dvacc[db], 0, 0, 0);
-        dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q, dsb[kk2], dkacc[db], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        pb[0][i] = static_cast<__bf16>(pv[i]);
+        pb[1][i] = static_cast<__bf16>(pv[8 + i]);
+        dsb[0][i] = static_cast<__bf16>(dsv[i]);
+        dsb[1][i] = static_cast<__bf16>(dsv[8 + i]);
       }
-    }
+      // dV^T += dO^T P, dK^T += Q^T dS (k = query rows, accumulator order).
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const int r_a = 16 * kk2 + tr_row, r_b = r_a + 8;
+        const int sw_a = qswz<D>(r_a), sw_b = qswz<D>(r_b);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
+          const int half = (tr_s & 1) * 8;
+          const int pa = r_a * L::QP + ((chunk ^ sw_a) << 4) + half;
+          const int pb_ = r_b * L::QP + ((chunk ^ sw_b) << 4) + half;
+          const bf16x8 a_do = lds_tr_pair(sdO + pa, sdO + pb_);
+          const bf16x8 a_q = lds_tr_pair(sQ + pa, sQ + pb_);
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_do, pb[kk2], dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q, dsb[kk2], dkacc[db], 0, 0, 0);
+        }
+      }
+    };
+    if (t0 >= kq_lo_max && t0 + kQB <= kq_hi_min)
+      finish(Stage<0>{});
+    else
+      finish(Stage<1>{});
     __builtin_amdgcn_s_waitcnt(0);  // direct loads of tile it+1 have landed in LDS
     __syncthreads();                // next Q/dO buffer ready
   };
@@ -309,16 +346,19 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     step(it, Stage<0>{});
     if (it + 1 < n_it) step(it + 1, Stage<1>{});
   }
+  if (n_it > 0 && !late) __builtin_amdgcn_s_barrier();
 
   // Sum the four heads' partials in a fixed order, (h0 + h2) + (h1 + h3),
   // through LDS (the tile buffers are free once every wave has left the
   // loop).  A wave's partial is stored lane-major, one float4 per lane per
   // step, so stores and loads are contiguous.
   __syncthreads();
-  float4* red = reinterpret_cast<float4*>(smem);
   constexpr int P4 = L::part / 16;  // float4 per wave partial
+  auto slot_ptr = [&](int slot_) {  // slots 0, 1 in stage 0; 2, 3 in stage 1
+    return reinterpret_cast<float4*>(slot_ < 2 ? stage0 : stage1) + (slot_ & 1) * P4;
+  };
   auto put = [&](int slot_) {
-    float4* p = red + slot_ * P4;
+    float4* p = slot_ptr(slot_);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -331,7 +371,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
       }
   };
   auto add = [&](int slot_) {
-    const float4* p = red + slot_ * P4;
+    const float4* p = slot_ptr(slot_);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -388,7 +428,7 @@ hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     bwd_dkdv_kernel<D><<<dim3(static_cast<unsigned>(grid)), 512, 0, st>>>(
         s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.lse, a.delta, m,
+        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.rowstat, m,
         static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

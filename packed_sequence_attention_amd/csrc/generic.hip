@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
                                                          const T* __restrict__ v,
                                                          const T* __restrict__ d_o,
                                                          const float* __restrict__ lse,
-                                                         const float* __restrict__ delta, MetaView m,
+                                                         const float* __restrict__ rowstat, MetaView m,
                                                          T* __restrict__ dq) {
   __shared__ float sq[kWaves][kMaxD];
   __shared__ float sdo[kWaves][kMaxD];
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
   const int lo = m.row_lo[bt], hi = m.row_hi[bt];
   const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
   const float lse_t = hi > lo ? lse[st] : 0.f;
-  const float delta_t = delta[st];
+  const float delta_t = rowstat[2 * st + 1];
   const int64_t kv_base = static_cast<int64_t>(b) * s.seq_len;
   float acc[NR];
 #pragma unroll
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
                                                           const T* __restrict__ v,
                                                           const T* __restrict__ d_o,
                                                           const float* __restrict__ lse,
-                                                          const float* __restrict__ delta, MetaView m,
+                                                          const float* __restrict__ rowstat, MetaView m,
                                                           T* __restrict__ dk, T* __restrict__ dv) {
   __shared__ float sk[kWaves][kMaxD];
   __shared__ float sv[kWaves][kMaxD];
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
         const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
         p = expf(s.scale * dot_row(sk[wave], q + row, D) - lse[st]);
         const float dp = dot_row(sv[wave], d_o + row, D);
-        ds = p * (dp - delta[st]);
+        ds = p * (dp - rowstat[2 * st + 1]);
       }
       sp[wave][lane] = p;
       sds[wave][lane] = ds;
@@ -263,13 +263,16 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
   }
 }
 
-// delta = sum_d dO * O in float32 for every (b, local row, query head).  A group of lpr
+// Row statistics of the backward for every (b, local row, query head):
+// delta = sum_d dO * O in float32, stored beside lse * log2(e) (the form the
+// matrix-core kernels exponentiate with) as one 8-byte pair.  A group of lpr
 // lanes (a power of two >= head_dim / 8) handles one row with 16-byte
 // accesses, so consecutive lanes touch consecutive memory.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnShape s, const T* __restrict__ o,
                                                        const T* __restrict__ d_o,
-                                                       float* __restrict__ delta, int lpr) {
+                                                       const float* __restrict__ lse,
+                                                       float* __restrict__ rowstat, int lpr) {
   const int64_t gtid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t idx = gtid / lpr;  // row (b, t, h), h fastest
   const int sub = static_cast<int>(gtid % lpr);
@@ -290,7 +293,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(AttnShape s, const T* __r
     const int64_t bt = idx / s.h_q;
     const int t = static_cast<int>(bt % s.q_len);
     const int b = static_cast<int>(bt / s.q_len);
-    delta[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t] = acc;
+    const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
+    *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse[st] * kLog2e, acc);
   }
 }
 
@@ -332,12 +336,12 @@ hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
   const int lpr = lanes_per_row(a.head_dim);
   bwd_prep_kernel<T><<<static_cast<unsigned>((rows * lpr + 255) / 256), 256, 0, st>>>(
-      s, static_cast<const T*>(a.o), static_cast<const T*>(a.d_o), a.delta, lpr);
+      s, static_cast<const T*>(a.o), static_cast<const T*>(a.d_o), a.lse, a.rowstat, lpr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dq_generic_kernel<T, NR><<<blocks_for(rows), 256, 0, st>>>(
       s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-      static_cast<const T*>(a.d_o), a.lse, a.delta, m, static_cast<T*>(a.dq));
+      static_cast<const T*>(a.d_o), a.lse, a.rowstat, m, static_cast<T*>(a.dq));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t keys = static_cast<int64_t>(a.batch) * a.seq_len * a.h_kv;
@@ -345,7 +349,7 @@ hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   dkv_generic_kernel<T, NR><<<blocks_for(keys), 256, 0, st>>>(
       s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-      static_cast<const T*>(a.d_o), a.lse, a.delta, m, static_cast<T*>(a.dk),
+      static_cast<const T*>(a.d_o), a.lse, a.rowstat, m, static_cast<T*>(a.dk),
       static_cast<T*>(a.dv));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -393,10 +397,10 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
   const unsigned grid = static_cast<unsigned>((rows * lpr + 255) / 256);
   if (a.dtype == 0)
     bwd_prep_kernel<float><<<grid, 256, 0, st>>>(s, static_cast<const float*>(a.o),
-                                                 static_cast<const float*>(a.d_o), a.delta, lpr);
+                                                 static_cast<const float*>(a.d_o), a.lse, a.rowstat, lpr);
   else
     bwd_prep_kernel<uint16_t><<<grid, 256, 0, st>>>(s, static_cast<const uint16_t*>(a.o),
-                                                    static_cast<const uint16_t*>(a.d_o), a.delta, lpr);
+                                                    static_cast<const uint16_t*>(a.d_o), a.lse, a.rowstat, lpr);
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // workspace: [batch][h_q][q_len]
+  float* rowstat;  // workspace: [batch][h_q][q_len] pairs (lse * log2(e), delta)
   hipEvent_t mark_start;  // recorded around the main kernel when non-null
   hipEvent_t mark_stop;
 };
@@ -58,10 +58,11 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 // one (batch row, K/V head)'s keys with 32-bit buffer offsets.
 bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim);
 bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim);
-// dQ of the matrix-core backward (query-stationary; needs delta).
+// dQ of the matrix-core backward (query-stationary; needs rowstat).
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
-// Backward row statistics: delta = rowsum(dO * O) in float32.
+// Backward row statistics: rowstat = (lse * log2(e), delta = rowsum(dO * O)),
+// float32.
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
 
 // Fill n 16-bit words with zeros (a kernel, so it is safe under graph capture).
