@@ -134,24 +134,34 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
   const int kv_stride = s.h_kv * D;
   const int kv_bytes = (s.seq_len * kv_stride - g * D) * 2;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + kv0), 0, kv_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + kv0), 0, kv_bytes, 0x00020000);
-  auto issue_tile = [&](int kt, int buf) {
+  // Direct load c (of 2 NCH: K and V chunks alternately) of key tile kt into
+  // stage buf.  The loads of the next tile are spread over the first S/dP
+  // block (one per step): issued together, a workgroup's loads queue up at
+  // the address unit and stall the waves.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // With live == false the load reads nothing (zero-sized resource) and
+  // writes zeros into the free stage: the loop issues it unconditionally, as
+  // a branch around it would split the S/dP block and stop the scheduler
+  // from overlapping its LDS reads with the products.
+  auto issue_chunk = [&](int kt, int buf, int c, bool live) {
     char* sK = buf == 0 ? stage0 : stage1;
-    char* sV = sK + kBN * RP;
-#pragma unroll
-    for (int i = 0; i < L::NCH; ++i) {
-      const int lc = i * 256 + tid;  // LDS chunk written by this lane
-      const int r = lc / CH, pc = lc % CH;
-      const int cch = pc ^ rswz<D>(r);
-      const int voff = ((kt * kBN + r) * kv_stride + cch * 8) * 2;
-      const int lbase = (i * 256 + wave * 64) * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(sK + lbase), 16, voff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(sV + lbase), 16, voff, 0, 0, 0);
-    }
+    char* dst = (c & 1) ? sK + kBN * RP : sK;
+    const int i = c >> 1;
+    // Lane index recomputed from an opaque mask (not hoisted, not spilled:
+    // a spilled copy's reload would wait on the direct loads in flight).
+    unsigned ones = ~0u;
+    asm volatile("" : "+s"(ones));
+    const int ln = static_cast<int>(__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u)));
+    const int lc = i * 256 + wave_u * 64 + ln;  // LDS chunk written by this lane
+    const int r = lc / CH, pc = lc % CH;
+    const int cch = pc ^ rswz<D>(r);
+    const int voff = ((kt * kBN + r) * kv_stride + cch * 8) * 2;
+    const int lbase = (i * 256 + wave_u * 64) * 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(((c & 1) ? v : k) + kv0), 0, live ? kv_bytes : 0, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + lbase), 16, voff, 0, 0, 0);
   };
+  static_assert(2 * L::NCH == KK, "one direct load per step of the first S/dP block");
 
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
@@ -159,13 +169,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
   if (kmax > kmin) {
     const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
-    issue_tile(kt0, 0);
+#pragma unroll
+    for (int c = 0; c < 2 * L::NCH; ++c) issue_chunk(kt0, 0, c, true);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Unrolled by two so that the stage is a compile-time constant.
     auto step = [&](int kt, auto stage) {
       constexpr int buf = decltype(stage)::value;
-      if (kt < kt1) issue_tile(kt + 1, buf ^ 1);  // that buffer was last read before the last barrier
+      const bool pre = kt < kt1;  // tile kt+1 goes to the other stage, last read before the last barrier
       const char* sK = buf == 0 ? stage0 : stage1;
       const char* sV = sK + kBN * RP;
       const int k0 = kt * kBN;
@@ -181,6 +192,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
           const int pos = rown * RP + (((2 * kk + kg) ^ nat_swz) << 4);
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + pos);
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(sV + pos);
+          if (sb == 0) issue_chunk(kt + 1, buf ^ 1, kk, pre);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], pacc, 0, 0, 0);
         }

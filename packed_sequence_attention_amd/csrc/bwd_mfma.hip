@@ -157,6 +157,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   const int wqlo = wave_min_i(qlo_k), wqhi = wave_max_i(qhi_k);
   // Rows inside every key's interval of this wave: [kq_lo_max, kq_hi_min).
   const int kq_lo_max = wave_max_i(qlo_k), kq_hi_min = wave_min_i(qhi_k);
+  // (Tested per tile as a per-lane compare: a uniform branch there makes the
+  // compiler restructure the loop and run out of registers.)
+  int kq_lo_v = kq_lo_max, kq_hi_v = kq_hi_min;
+  asm volatile("" : "+v"(kq_lo_v), "+v"(kq_hi_v));
   // Element mask: row t is allowed iff (unsigned)(t - mask_lo) < mask_span.
   const int mask_lo = qhi_k > qlo_k ? qlo_k : 0;
   const unsigned mask_span = qhi_k > qlo_k ? static_cast<unsigned>(qhi_k - qlo_k) : 0u;
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
         }
       }
     };
-    if (t0 >= kq_lo_max && t0 + kQB <= kq_hi_min)
+    if (t0 >= kq_lo_v && t0 + kQB <= kq_hi_v)
       finish(Stage<0>{});
     else
       finish(Stage<1>{});

@@ -57,15 +57,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+// Wave-wide min / max (all 64 lanes active).  Every lane holds the result
+// after the butterfly; reading it from the first lane marks it uniform, so
+// it can feed scalar registers (buffer resources, loop bounds).
 __device__ __forceinline__ int wave_min_i(int x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
-  return x;
+  return __builtin_amdgcn_readfirstlane(x);
 }
 __device__ __forceinline__ int wave_max_i(int x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  return x;
+  return __builtin_amdgcn_readfirstlane(x);
 }
 
 // Launch parameters.  Sizes are int32 (checked on the host); element
