@@ -24,6 +24,12 @@
 //   O^T += V^T P^T: B = P straight from the accumulator (bf16), A = V^T read
 //   with the LDS transpose load (ds_read_b64_tr_b16) from row-major V, with
 //   the key order of the accumulator; O^T accumulates in registers.
+// K / V tiles reach LDS by direct global -> LDS loads (buffer form: keys past
+// the row read as zero) into a two-stage buffer; the loads of the next tile
+// are spread over the first S block.  Rows are stored without padding, the
+// 16-byte chunk c of row r at chunk c ^ f(r), which keeps both the row reads
+// (16 rows, one chunk) and the transpose reads (4 rows x 4 chunks) free of
+// bank conflicts.
 // Softmax in base 2 with scale*log2(e) folded in; the running max is only
 // raised when it grows by more than 8 (a factor 256), which keeps every
 // exponent <= 2^8 and skips most accumulator rescales; the result is the
@@ -42,16 +48,26 @@ constexpr int kBM = 32;  // query rows per workgroup (one per lane pair)
 
 template <int D>
 struct FwdLds {
-  static constexpr int KP = D * 2 + 16;  // K row pitch (bytes): 16-byte skew per row
-  static constexpr int VP = D * 2 + 64;  // V row pitch: rows of a transpose read hit distinct banks
-  static constexpr int buf = kBN * (KP + VP);  // one K/V tile
-  static constexpr int bytes = 2 * buf;        // double buffered
-  static constexpr int NCH = kBN * (D / 8) / 256;  // 16-byte chunks per thread per tensor
+  static constexpr int RP = D * 2;                 // row pitch (bytes), swizzled chunks
+  static constexpr int tile = 2 * kBN * RP;        // K tile then V tile (one stage)
+  static constexpr int NCH = kBN * (D / 8) / 256;  // direct loads per thread per tensor
 };
 
-__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, int second_off) {
+// Chunk swizzle of row r of a K / V tile.
+template <int D>
+__device__ __forceinline__ int rswz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int B>
+struct Stage {
+  static constexpr int value = B;
+};
+
+__device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + second_off));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
   const auto ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
@@ -64,11 +80,15 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
                                                           float* __restrict__ lse, int n_qt, int n_hg) {
   constexpr int KK = D / 16;  // k-steps of Q K^T
   constexpr int DB = D / 32;  // 32-wide blocks of O^T
-  constexpr int KP = FwdLds<D>::KP;
-  constexpr int VP = FwdLds<D>::VP;
   constexpr int CH = D / 8;   // 16-byte chunks per K/V row
-  constexpr int NCH = FwdLds<D>::NCH;
-  __shared__ __attribute__((aligned(16))) char smem[FwdLds<D>::bytes];
+  using L = FwdLds<D>;
+  constexpr int RP = L::RP;
+  // The two stages are separate LDS objects: the compiler then knows that
+  // the direct loads into one stage do not alias reads of the other, and
+  // does not make those reads wait for the loads in flight.
+  __shared__ __attribute__((aligned(16))) char stage0[L::tile];
+  __shared__ __attribute__((aligned(16))) char stage1[L::tile];
+  typedef __attribute__((address_space(3))) void lds_void;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
@@ -118,50 +138,50 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
   float mrun = -INFINITY, lrun = 0.f;
   const float c = s.scale * kLog2e;
 
-  // Per-lane LDS offsets.
-  const int k_rd = n * KP + kg * 16;
-  const int v_rd = (4 * kg + ((lane & 15) >> 2)) * VP + (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  // Direct load c (of 2 NCH: K and V chunks alternately) of key tile kt into
+  // stage buf.  With live == false the load reads nothing (zero-sized
+  // resource) and writes zeros into the free stage: it is issued without a
+  // branch, which would split the S block and stop the scheduler from
+  // overlapping its LDS reads with the products.
+  const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
+  const int kv_stride = s.h_kv * D;
+  const int kv_bytes = (s.seq_len * kv_stride - g * D) * 2;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_chunk = [&](int kt, int buf, int c, bool live) {
+    char* sK = buf == 0 ? stage0 : stage1;
+    char* dst = (c & 1) ? sK + kBN * RP : sK;
+    const int i = c >> 1;
+    // Lane index recomputed from an opaque mask (not hoisted, not spilled:
+    // a spilled copy's reload would wait on the direct loads in flight).
+    unsigned ones = ~0u;
+    asm volatile("" : "+s"(ones));
+    const int ln = static_cast<int>(__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u)));
+    const int lc = i * 256 + wave_u * 64 + ln;  // LDS chunk written by this lane
+    const int r = lc / CH, pc = lc % CH;
+    const int voff = ((kt * kBN + r) * kv_stride + (pc ^ rswz<D>(r)) * 8) * 2;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(((c & 1) ? v : k) + kv0), 0, live ? kv_bytes : 0, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16, voff,
+                                             0, 0, 0);
+  };
+  static_assert(2 * L::NCH == KK, "one direct load per step of the first S block");
 
-  // K/V tile staging: global -> registers (issued one tile ahead) -> LDS.
-  uint4 kx[NCH], vx[NCH];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CH, col = ci % CH;
-      const int j = kt * kBN + r;
-      kx[i] = make_uint4(0, 0, 0, 0);
-      vx[i] = make_uint4(0, 0, 0, 0);
-      if (j < s.seq_len) {
-        const int64_t off = ((static_cast<int64_t>(b) * s.seq_len + j) * s.h_kv + g) * D + col * 8;
-        kx[i] = *reinterpret_cast<const uint4*>(k + off);
-        vx[i] = *reinterpret_cast<const uint4*>(v + off);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* sK = smem + buf * FwdLds<D>::buf;
-    char* sV = sK + kBN * KP;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ci = tid + 256 * i;
-      const int r = ci / CH, col = ci % CH;
-      *reinterpret_cast<uint4*>(sK + r * KP + col * 16) = kx[i];
-      *reinterpret_cast<uint4*>(sV + r * VP + col * 16) = vx[i];
-    }
-  };
+  const int nat_swz = rswz<D>(n);
+  const int tr_row = 4 * kg + ((lane & 15) >> 2);
+  const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
 
   if (kmax > kmin) {
     const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
-    load_tile(kt0);
-    store_tile(0);
+#pragma unroll
+    for (int cc = 0; cc < 2 * L::NCH; ++cc) issue_chunk(kt0, 0, cc, true);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = kt0; kt <= kt1; ++kt) {
-      const int buf = (kt - kt0) & 1;
-      const bool more = kt < kt1;
-      if (more) load_tile(kt + 1);  // in flight during this tile's math
-      const char* sK = smem + buf * FwdLds<D>::buf;
-      const char* sV = sK + kBN * KP;
+    // Unrolled by two so that the stage is a compile-time constant.
+    auto step = [&](int kt, auto stage) {
+      constexpr int buf = decltype(stage)::value;
+      const bool pre = kt < kt1;  // tile kt+1 goes to the other stage, last read before the last barrier
+      const char* sK = buf == 0 ? stage0 : stage1;
+      const char* sV = sK + kBN * RP;
       const int k0 = kt * kBN;
       const bool full = all_real && lomax <= k0 && k0 + kBN - 1 <= pfirst;
 #pragma unroll
@@ -169,11 +189,14 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
         f32x16 sacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+        const int rown = sb * 32 + n;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + sb * 32 * KP + k_rd + kk * 32);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + rown * RP + (((2 * kk + kg) ^ nat_swz) << 4));
+          if (sb == 0) issue_chunk(kt + 1, buf ^ 1, kk, pre);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
         }
+        // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
         if (!full) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
@@ -211,18 +234,27 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
           pb[0][i] = static_cast<__bf16>(p[i]);
           pb[1][i] = static_cast<__bf16>(p[8 + i]);
         }
+        // O^T += V^T P^T: A = V^T (rows = keys in accumulator order).
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const char* vb = sV + (sb * 32 + 16 * kk2) * VP + v_rd;
+          const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
+          const int swa = rswz<D>(ra), swb = rswz<D>(rb);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x8 va = lds_tr_pair(vb + db * 64, 8 * VP);
+            const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
+            const int half = (tr_s & 1) * 8;
+            const bf16x8 va = lds_tr_pair(sV + ra * RP + ((chunk ^ swa) << 4) + half,
+                                          sV + rb * RP + ((chunk ^ swb) << 4) + half);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk2], oacc[db], 0, 0, 0);
           }
         }
       }
-      if (more) store_tile(buf ^ 1);  // that buffer was last read before the previous barrier
+      __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
       __syncthreads();
+    };
+    for (int kt = kt0; kt <= kt1; kt += 2) {
+      step(kt, Stage<0>{});
+      if (kt + 1 <= kt1) step(kt + 1, Stage<1>{});
     }
   }
 
