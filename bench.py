@@ -87,10 +87,10 @@ def kernel_source_digest(name):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_file, workload_tag):
+def traffic_from_profile(kernel, kernel_file, workload_tag):
     """HBM bytes per launch from profiles/<kernel>_<workload>_traffic.md when
     its recorded source digest matches the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_file.split('.')[0]}_{workload_tag}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -229,7 +229,7 @@ def main():
     value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
     flops_dkdv = 8 * D * Hq * pairs
     achieved = flops_dkdv / (bwd_avg * 1e-3) / 1e12
-    traffic = traffic_from_profile("bwd_mfma.hip", f"w{args.workload}") if w.dtype == "bf16" else None
+    traffic = traffic_from_profile("bwd_dkdv", "bwd_mfma.hip", f"w{args.workload}") if w.dtype == "bf16" else None
     out = {
         "metric": METRIC,
         "value": round(value, 3),
