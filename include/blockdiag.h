@@ -188,7 +188,8 @@ bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
  *   gives the full gradient (Design overview, exchange.py: the K/V gradient
  *   is reduce-scattered with SUM).
  *   workspace: at least blockdiag_workspace_bytes(1, ...) bytes of device
- *   memory (the float32 row statistic delta = rowsum(dO * O)).
+ *   memory (float32 row statistics: lse * log2(e) and delta = rowsum(dO * O)
+ *   per row and query head, 8 bytes each).
  * The backward is bitwise deterministic (no atomics): each of dQ, dK, dV is
  * written once by the workgroup that owns its rows or keys.
  * Errors: as blockdiag_attn_fwd.
