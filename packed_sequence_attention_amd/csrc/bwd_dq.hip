@@ -2,7 +2,9 @@
 // for gfx950 (query-stationary).
 //
 // Automodel page "feat(distributed): block-diagonal varlen CP for packed
-// sequences", Proof section (input gradients).  For each local row i:
+// sequences", Proof section (input gradients).  The kernel also produces the
+// row statistics (lse * log2(e), delta_i = dO_i . O_i) that the dK/dV kernel
+// reads.  For each local row i:
 //   P_ij  = exp(scale q_i.k_j - LSE_i),  dP_ij = dO_i . v_j,
 //   dS_ij = P_ij (dP_ij - delta_i),      dQ_i = scale sum_j dS_ij k_j
 // over the keys j of row i's document up to i.
@@ -63,8 +65,9 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
-    const float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dq, int n_qt, int n_hg) {
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ o,
+    const float* __restrict__ lse, float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dq,
+    int n_qt, int n_hg) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
@@ -92,14 +95,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const bool valid = t < s.q_len;
   const int64_t bt = static_cast<int64_t>(b) * s.q_len + t;
   int lo = 0, hi = 0;
-  float lse2 = 0.f, dlt = 0.f;
+  float lse2 = 0.f;
+  const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
   if (valid) {
     lo = m.row_lo[bt];
     hi = m.row_hi[bt];
-    const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
-    const float2 rs = *reinterpret_cast<const float2*>(rowstat + 2 * st);
-    lse2 = rs.x;  // lse * log2(e); -inf on padding rows: masked below
-    dlt = rs.y;
+    lse2 = lse[st] * kLog2e;  // -inf on padding rows: masked below
   }
   const bool real = hi > lo;
   const int kmin = wave_min_i(real ? lo : INT_MAX);
@@ -122,6 +123,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       }
     }
   }
+  // Row statistic delta = dO . O (float32): this lane's half of the row, then
+  // the partner lane's.  The (lse * log2(e), delta) pair is also written for
+  // the dK/dV kernel, which runs after this one.
+  float dlt = 0.f;
+  if (valid) {
+    const int64_t row = (bt * s.h_q + h) * D + kg * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row + kk * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dlt = fmaf(static_cast<float>(of[kk][i]), static_cast<float>(ov[i]), dlt);
+    }
+  }
+  dlt += __shfl_xor(dlt, 32, 64);
+  if (valid && kg == 0) *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse2, dlt);
 
   f32x16 dqacc[DB];
 #pragma unroll
@@ -263,8 +279,8 @@ hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
   const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
   bwd_dq_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.rowstat, m,
-      static_cast<uint16_t*>(a.dq), n_qt, n_hg);
+      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o),
+      static_cast<const uint16_t*>(a.o), a.lse, a.rowstat, m, static_cast<uint16_t*>(a.dq), n_qt, n_hg);
   return hipGetLastError();
 }
 

@@ -422,7 +422,8 @@ hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
   s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
   s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
-  hipError_t e = launch_bwd_prep(a, st);
+  // The dQ kernel runs first: it also writes the row statistics.
+  hipError_t e = launch_bwd_dq(a, st);
   if (e != hipSuccess) return e;
   const int n_kt = (a.seq_len + kKB - 1) / kKB;
   const int n_bg = a.batch * a.h_kv;
@@ -439,7 +440,7 @@ hipError_t bwd_mfma_t(const BwdArgs& a, hipStream_t st) {
     e = mark(a.mark_stop, st);
     if (e != hipSuccess) return e;
   }
-  return launch_bwd_dq(a, st);
+  return hipSuccess;
 }
 
 }  // namespace

@@ -58,7 +58,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 // one (batch row, K/V head)'s keys with 32-bit buffer offsets.
 bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim);
 bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim);
-// dQ of the matrix-core backward (query-stationary; needs rowstat).
+// dQ of the matrix-core backward (query-stationary); also writes rowstat.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 
 // Backward row statistics: rowstat = (lse * log2(e), delta = rowsum(dO * O)),
