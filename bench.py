@@ -101,35 +101,34 @@ def traffic_from_profile(kernel, kernel_file, workload_tag):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, t, flops_per_pair, budget_units=None):
-    """The fp64 oracle (windowed, unchanged) on a bounded sample: the first
-    `budget_units` (batch row, K/V head) sub-problems of the workload, each a
-    K/V head's query-head group over the whole row, forward and backward, in
-    a pool of worker processes with one BLAS thread each."""
+def cpu_baseline(w, t, flops_per_pair, budget_s=10.0):
+    """The fp64 oracle (windowed, unchanged) timed on this host: batch rows
+    are run one after another (each row's K/V heads as sub-problems over the
+    whole row, forward and backward, in a pool of worker processes with one
+    BLAS thread each) until the rows done so far have taken `budget_s`
+    seconds or the whole workload is done."""
     import numpy as np
     from oracle import parallel
-    B, Hkv = w.batch, w.h_kv
-    units = [(b, g) for b in range(B) for g in range(Hkv)]
-    n_units = budget_units or len(units)
-    G = w.h_q // w.h_kv
-    # the sample: batch row 0, K/V heads 0..n-1 (contiguous slices of the same tensors)
-    n_heads = min(n_units, Hkv)
-    sub_q = np.ascontiguousarray(t["q"][:1, :, :n_heads * G])
-    sub_do = np.ascontiguousarray(t["do"][:1, :, :n_heads * G])
-    sub_k = np.ascontiguousarray(t["k"][:1, :, :n_heads])
-    sub_v = np.ascontiguousarray(t["v"][:1, :, :n_heads])
-    workers = parallel.default_workers()
-    t0 = time.perf_counter()
-    parallel.run(sub_q, sub_k, sub_v, sub_do, w.doc_lens[:1], w.row_offset, w.scale, block_rows=256,
-                 workers=workers)
-    dt = time.perf_counter() - t0
     from oracle import attention as A
-    pairs = A.useful_pairs(w.doc_lens[:1], w.seq_len, w.row_offset, w.q_len)
-    flops = flops_per_pair * n_heads * G * pairs
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(workers, n_heads),
+    workers = parallel.default_workers()
+    dt = 0.0
+    flops = 0
+    rows = 0
+    for b in range(w.batch):
+        sub = {k: np.ascontiguousarray(t[k][b:b + 1]) for k in ("q", "k", "v", "do")}
+        t0 = time.perf_counter()
+        parallel.run(sub["q"], sub["k"], sub["v"], sub["do"], w.doc_lens[b:b + 1], w.row_offset, w.scale,
+                     block_rows=256, workers=workers)
+        dt += time.perf_counter() - t0
+        pairs = A.useful_pairs(w.doc_lens[b:b + 1], w.seq_len, w.row_offset, w.q_len)
+        flops += flops_per_pair * w.h_q * pairs
+        rows += 1
+        if dt >= budget_s:
+            break
+    what = "the whole workload" if rows == w.batch else f"batch rows 0..{rows - 1} of {w.batch}"
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(workers, w.h_kv),
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"batch row 0, K/V heads 0..{n_heads - 1} ({n_heads * G} query heads) of the "
-                      f"workload, forward+backward, fp64 numpy windowed oracle"}
+            "sample": f"{what} (all {w.h_q} query heads), forward+backward, fp64 numpy windowed oracle"}
 
 
 def main():
