@@ -159,23 +159,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   // writes zeros into the free stage: the loop issues it unconditionally, as
   // a branch around it would split the S/dP block and stop the scheduler
   // from overlapping its LDS reads with the products.
+  // Per-lane part of the offsets of load i (K and V tiles share it); the
+  // tile's row offset goes into the resource base.
+  int dma_off[L::NCH];
+#pragma unroll
+  for (int i = 0; i < L::NCH; ++i) {
+    const int lc = i * 256 + wave_u * 64 + lane;  // LDS chunk written by this lane
+    const int r = lc / CH, pc = lc % CH;
+    dma_off[i] = (r * kv_stride + (pc ^ rswz<D>(r)) * 8) * 2;
+  }
   auto issue_chunk = [&](int kt, int buf, int c, bool live) {
     char* sK = buf == 0 ? stage0 : stage1;
     char* dst = (c & 1) ? sK + kBN * RP : sK;
     const int i = c >> 1;
-    // Lane index recomputed from an opaque mask (not hoisted, not spilled:
-    // a spilled copy's reload would wait on the direct loads in flight).
-    unsigned ones = ~0u;
-    asm volatile("" : "+s"(ones));
-    const int ln = static_cast<int>(__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u)));
-    const int lc = i * 256 + wave_u * 64 + ln;  // LDS chunk written by this lane
-    const int r = lc / CH, pc = lc % CH;
-    const int cch = pc ^ rswz<D>(r);
-    const int voff = ((kt * kBN + r) * kv_stride + cch * 8) * 2;
-    const int lbase = (i * 256 + wave_u * 64) * 16;
+    const int tile_off = kt * kBN * kv_stride;  // elements
+    const int vo = dma_off[i];
+    const int nbytes = live ? kv_bytes - tile_off * 2 : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(((c & 1) ? v : k) + kv0), 0, live ? kv_bytes : 0, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + lbase), 16, voff, 0, 0, 0);
+        const_cast<uint16_t*>(((c & 1) ? v : k) + kv0 + tile_off), 0, nbytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16,
+                                             vo, 0, 0, 0);
   };
   static_assert(2 * L::NCH == KK, "one direct load per step of the first S/dP block");
 
