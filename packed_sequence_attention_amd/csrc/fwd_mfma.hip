@@ -11,7 +11,7 @@
 //   query rows); wave w owns query head 4*hg + w for those 32 rows, so all
 //   four waves share every K/V tile staged in LDS (grouped-query reuse) and
 //   have the same live key range.
-//   Key tiles are 64 keys anchored at multiples of 64 in the row; only tiles
+//   Key tiles are 32 keys anchored at multiples of 32 in the row; only tiles
 //   in [doc_start(first real row), last real row] are visited (every one of
 //   them holds an allowed pair), and the element mask is applied only on
 //   tiles that are not entirely allowed.
@@ -26,10 +26,11 @@
 //   the key order of the accumulator; O^T accumulates in registers.
 // K / V tiles reach LDS by direct global -> LDS loads (buffer form: keys past
 // the row read as zero) into a two-stage buffer; the loads of the next tile
-// are spread over the first S block.  Rows are stored without padding, the
-// 16-byte chunk c of row r at chunk c ^ f(r), which keeps both the row reads
-// (16 rows, one chunk) and the transpose reads (4 rows x 4 chunks) free of
-// bank conflicts.
+// are spread over the tile's S products.  32-key tiles keep a workgroup's
+// LDS at 32 KB, so three workgroups (three waves per SIMD) fit on a CU.
+// Rows are stored without padding, the 16-byte chunk c of row r at chunk
+// c ^ f(r), which keeps both the row reads (16 rows, one chunk) and the
+// transpose reads (4 rows x 4 chunks) free of bank conflicts.
 // Softmax in base 2 with scale*log2(e) folded in; the running max is only
 // raised when it grows by more than 8 (a factor 256), which keeps every
 // exponent <= 2^8 and skips most accumulator rescales; the result is the
@@ -43,7 +44,7 @@
 namespace bd {
 namespace {
 
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = 32;  // keys per tile
 constexpr int kBM = 32;  // query rows per workgroup (one per lane pair)
 
 template <int D>
@@ -73,7 +74,7 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, MetaView m,
                                                           uint16_t* __restrict__ o,
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16,
                                              vo, 0, 0, 0);
   };
-  static_assert(2 * L::NCH == KK, "one direct load per step of the first S block");
+  static_assert(2 * L::NCH <= KK, "at most one direct load per step of the first S block");
 
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void fwd_mfma_kernel(AttnShape s, const uin
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + rown * RP + (((2 * kk + kg) ^ nat_swz) << 4));
-          if (sb == 0) issue_chunk(kt + 1, buf ^ 1, kk, pre);
+          if (sb == 0 && kk < 2 * L::NCH) issue_chunk(kt + 1, buf ^ 1, kk, pre);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
         }
         // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
