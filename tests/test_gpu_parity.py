@@ -185,3 +185,35 @@ def test_workload4_sampled_parity_and_invariants():
         rhs = do[0, :, gh * G:(gh + 1) * G].sum((0, 1))
         assert np.linalg.norm(lhs - rhs) <= 1e-2 * np.linalg.norm(rhs) + 1e-3
     _log("  errors", errs, {"dq": e_dq, "dk": e_dk, "dv": e_dv})
+
+
+@gpu
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_single_document_spanning_every_chunk(dtype, d):
+    """One document fills the row and is split into 4 contiguous chunks (the
+    context-parallel layout of the Automodel page's Design overview): every
+    chunk after the first has a long asymmetric first segment (more keys than
+    queries).  Each chunk's O, LSE and dQ match the oracle on its rows, and
+    the chunks' partial dK/dV summed over the chunks match the oracle's
+    gradients of the whole row (what the reduce-scatter of dK/dV returns)."""
+    S, cp = 1536, 4
+    w_full, t = H.small_case(400 + d, dtype, [[S]], S, 0, S, 8, 2, d)
+    full = H.oracle(w_full, t, block_rows=256)
+    L = S // cp
+    dk_sum = np.zeros_like(full["dk"])
+    dv_sum = np.zeros_like(full["dv"])
+    for c in range(cp):
+        a = c * L
+        wc = synthetic.custom_workload(400 + d, dtype, [[S]], S, a, L, 8, 2, d, name=f"chunk{c}")
+        tc = {"q": t["q"][:, a:a + L], "k": t["k"], "v": t["v"], "do": t["do"][:, a:a + L]}
+        _log(f"single document {dtype} d={d}: chunk {c} rows [{a}, {a + L})")
+        g = H.run_gpu(wc, tc)
+        ref_c = {"o": full["o"][:, a:a + L], "lse": full["lse"][:, :, a:a + L], "dq": full["dq"][:, a:a + L]}
+        errs = H.check(wc, {"o": g["o"], "lse": g["lse"], "dq": g["dq"], "dk": g["dk"], "dv": g["dv"]},
+                       {**ref_c, "dk": g["dk"], "dv": g["dv"]})
+        _log("  errors", {k: f"{v:.3g}" for k, v in errs.items() if k not in ("dk", "dv")})
+        dk_sum += g["dk"]
+        dv_sum += g["dv"]
+    errs = H.check(w_full, {"dk": dk_sum, "dv": dv_sum, "dq": full["dq"]},
+                   {"dk": full["dk"], "dv": full["dv"], "dq": full["dq"]})
+    _log("  summed dK/dV errors", {k: f"{v:.3g}" for k, v in errs.items() if k != "dq"})
