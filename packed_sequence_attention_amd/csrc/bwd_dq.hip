@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   if (valid) {
     lo = m.row_lo[bt];
     hi = m.row_hi[bt];
-    lse2 = lse[st] * kLog2e;  // -inf on padding rows: masked below
+    lse2 = lse[st] * kLog2e;  // -inf on padding rows
   }
   const bool real = hi > lo;
   const int kmin = wave_min_i(real ? lo : INT_MAX);
@@ -145,6 +145,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqacc[db][j] = 0.f;
   const float c = s.scale * kLog2e;
+  // Rows with no allowed key (padding, past the chunk) take +inf, so every
+  // P of theirs is exp2(-inf) = 0 (with -inf from the rows' own LSE the
+  // masked -inf - (-inf) would be NaN).
+  const float lse2m = real ? lse2 : INFINITY;
 
   // Direct loads of key tile kt into buffer buf (keys past the row read 0).
   const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
@@ -216,14 +220,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], pacc, 0, 0, 0);
         }
         // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
+        // The mask is one block over the whole accumulator (S = -inf, so
+        // P = 0): a test inside the exp loop would be split into one branch
+        // per element and keep the exps from overlapping the products.
+        if (!full) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int key = k0 + sb * 32 + (j >> 2) * 8 + kg * 4 + (j & 3);
+            if (key < lo || key >= hi) sacc[j] = -INFINITY;
+          }
+        }
         float dsv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lse2));
-          if (!full) {
-            const int key = k0 + sb * 32 + (j >> 2) * 8 + kg * 4 + (j & 3);
-            p = (key >= lo && key < hi) ? p : 0.f;  // a select: also clears inf on padding rows
-          }
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lse2m));
           dsv[j] = p * (pacc[j] - dlt);
         }
         bf16x8 dsb[2];
