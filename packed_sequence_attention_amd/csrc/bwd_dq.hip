@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       for (int i = 0; i < 8; ++i) dlt = fmaf(static_cast<float>(of[kk][i]), static_cast<float>(ov[i]), dlt);
     }
   }
-  dlt += __shfl_xor(dlt, 32, 64);
+  dlt = pair32_sum(dlt);
   if (valid && kg == 0) *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse2, dlt);
 
   f32x16 dqacc[DB];

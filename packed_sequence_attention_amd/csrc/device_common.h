@@ -57,6 +57,19 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+// Lane l and lane l ^ 32 combined (all 64 lanes active): v_permlane32_swap
+// exchanges the upper half of one register with the lower half of the other,
+// so after swapping x with itself every lane holds both values of its pair.
+// A VALU exchange, without the LDS round trip of a bpermute.
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wave-wide min / max (all 64 lanes active).  Every lane holds the result
 // after the butterfly; reading it from the first lane marks it uniform, so
 // it can feed scalar registers (buffer resources, loop bounds).

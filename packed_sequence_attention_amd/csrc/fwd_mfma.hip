@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
         float mx = sacc[0];
 #pragma unroll
         for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = pair32_max(mx);
         const float mnew = fmaxf(mrun, mx * c);
         const bool need = mnew > mrun + 8.f;
         if (__any(need)) {
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
     }
   }
 
-  const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+  const float ltot = pair32_sum(lrun);
   if (valid) {
     const bool any = ltot > 0.f;
     const float inv = any ? 1.f / ltot : 0.f;
