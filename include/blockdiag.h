@@ -151,6 +151,23 @@ bd_status blockdiag_meta_build(const int32_t *d_table, int32_t n_seg, int32_t ba
                                int32_t *d_meta, void *stream);
 
 /*
+ * blockdiag_meta_build_host -- blockdiag_meta_build for a table in host
+ * memory (h_table, same layout as d_table) of at most
+ * blockdiag_meta_inline_max_seg() segments: the table is read on the host
+ * during the call and travels to the kernel in its launch arguments, so the
+ * step needs no host-to-device copy of it (Summary: per-step precompute,
+ * zero per-layer host syncs).  h_table is not retained after the call
+ * returns.  d_meta, the output and the stream ordering are as for
+ * blockdiag_meta_build.  Errors: BD_ERR_CAPACITY when n_seg exceeds the
+ * limit (nothing is launched; use blockdiag_meta_build), BD_ERR_INVALID_ARG,
+ * BD_ERR_BAD_METADATA, BD_ERR_HIP.
+ */
+int32_t blockdiag_meta_inline_max_seg(void);
+bd_status blockdiag_meta_build_host(const int32_t *h_table, int32_t n_seg, int32_t batch,
+                                    int32_t seq_len, int32_t row_offset, int32_t q_len,
+                                    int32_t *d_meta, void *stream);
+
+/*
  * blockdiag_workspace_bytes -- device scratch the forward (is_bwd = 0) or
  * backward (is_bwd = 1) needs for these sizes (0 is a valid answer).
  */

@@ -45,6 +45,7 @@ _LIB = None
 STATUS = {0: "BD_OK", 1: "BD_ERR_INVALID_ARG", 2: "BD_ERR_BAD_METADATA", 3: "BD_ERR_CAPACITY",
           4: "BD_ERR_WORKSPACE", 5: "BD_ERR_UNSUPPORTED", 6: "BD_ERR_HIP"}
 EXPORTS = ("blockdiag_segment", "blockdiag_validate", "blockdiag_meta_ints", "blockdiag_meta_build",
+           "blockdiag_meta_build_host", "blockdiag_meta_inline_max_seg",
            "blockdiag_workspace_bytes", "blockdiag_attn_fwd", "blockdiag_attn_bwd",
            "blockdiag_mark_main_kernel", "blockdiag_last_error", "blockdiag_version")
 
@@ -79,6 +80,10 @@ def load_library():
     lib.blockdiag_meta_ints.restype = sz
     lib.blockdiag_meta_build.argtypes = [p, i32, i32, i32, i32, i32, p, p]
     lib.blockdiag_meta_build.restype = ctypes.c_int
+    lib.blockdiag_meta_build_host.argtypes = [pi32, i32, i32, i32, i32, i32, p, p]
+    lib.blockdiag_meta_build_host.restype = ctypes.c_int
+    lib.blockdiag_meta_inline_max_seg.argtypes = []
+    lib.blockdiag_meta_inline_max_seg.restype = i32
     lib.blockdiag_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, i32, i32, i32]
     lib.blockdiag_workspace_bytes.restype = sz
     lib.blockdiag_attn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
@@ -129,16 +134,26 @@ class SegTable:
     meta: object = None
     _pinned: object = None
 
-    def to(self, device):
-        """Upload the table and build the device metadata on ``device``."""
+    def to(self, device, inline=None):
+        """Build the device metadata on ``device``.  A table of at most
+        ``blockdiag_meta_inline_max_seg()`` segments goes to the kernel in its
+        launch arguments (``blockdiag_meta_build_host``, no upload); a larger
+        one (or ``inline=False``) is copied to the device first
+        (``blockdiag_meta_build``)."""
         import torch
         lib = load_library()
-        host = torch.from_numpy(np.concatenate([self.cu_q, self.cu_k, self.k_begin]).astype(np.int32))
-        pinned = host.pin_memory()
-        table = pinned.to(device, non_blocking=True)  # no host sync; pinned copy kept alive below
+        flat = np.ascontiguousarray(np.concatenate([self.cu_q, self.cu_k, self.k_begin]), dtype=np.int32)
         n_meta = lib.blockdiag_meta_ints(self.batch, self.seq_len, self.q_len)
         meta = torch.empty(max(int(n_meta), 1), dtype=torch.int32, device=device)
         stream = torch.cuda.current_stream(device).cuda_stream
+        if inline is None:
+            inline = self.n_seg <= lib.blockdiag_meta_inline_max_seg()
+        if inline:
+            _check(lib.blockdiag_meta_build_host(_ptr(flat), self.n_seg, self.batch, self.seq_len,
+                                                 self.row_offset, self.q_len, meta.data_ptr(), stream))
+            return dataclasses.replace(self, table=None, meta=meta, _pinned=None)
+        pinned = torch.from_numpy(flat).pin_memory()
+        table = pinned.to(device, non_blocking=True)  # no host sync; pinned copy kept alive below
         _check(lib.blockdiag_meta_build(table.data_ptr(), self.n_seg, self.batch, self.seq_len,
                                         self.row_offset, self.q_len, meta.data_ptr(), stream))
         return dataclasses.replace(self, table=table, meta=meta, _pinned=pinned)

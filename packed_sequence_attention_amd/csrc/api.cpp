@@ -90,7 +90,31 @@ extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, int32_t n_seg,
   if (d_table == nullptr || d_meta == nullptr) return fail(BD_ERR_INVALID_ARG, "null pointer");
   if (n_seg == 0 && static_cast<int64_t>(batch) * q_len > 0)
     return fail(BD_ERR_BAD_METADATA, "empty segment table for a non-empty chunk");
-  hipError_t e = bd::launch_meta_build(d_table, n_seg, batch, seq_len, row_offset, q_len, d_meta,
+  hipError_t e = bd::launch_meta_build(d_table, false, n_seg, batch, seq_len, row_offset, q_len, d_meta,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
+  return BD_OK;
+}
+
+extern "C" int32_t blockdiag_meta_inline_max_seg(void) { return bd::kInlineSeg; }
+
+extern "C" bd_status blockdiag_meta_build_host(const int32_t* h_table, int32_t n_seg, int32_t batch,
+                                               int32_t seq_len, int32_t row_offset, int32_t q_len,
+                                               int32_t* d_meta, void* stream) {
+  bd::clear_error();
+  if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0 || n_seg < 0)
+    return fail(BD_ERR_INVALID_ARG, "negative size");
+  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
+    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
+  if (static_cast<int64_t>(batch) * seq_len > kMaxElems) return fail(BD_ERR_INVALID_ARG, "too large");
+  if (n_seg > bd::kInlineSeg)
+    return fail(BD_ERR_CAPACITY, "%d segments: at most %d pass by value (use blockdiag_meta_build)", n_seg,
+                bd::kInlineSeg);
+  if (blockdiag_meta_ints(batch, seq_len, q_len) == 0) return BD_OK;
+  if (h_table == nullptr || d_meta == nullptr) return fail(BD_ERR_INVALID_ARG, "null pointer");
+  if (n_seg == 0 && static_cast<int64_t>(batch) * q_len > 0)
+    return fail(BD_ERR_BAD_METADATA, "empty segment table for a non-empty chunk");
+  hipError_t e = bd::launch_meta_build(h_table, true, n_seg, batch, seq_len, row_offset, q_len, d_meta,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
   return BD_OK;

@@ -42,8 +42,12 @@ struct BwdArgs {
   hipEvent_t mark_stop;
 };
 
-// Metadata expansion (segment table -> per-row / per-key bounds).
-hipError_t launch_meta_build(const int32_t* d_table, int n_seg, int batch, int seq_len,
+// Metadata expansion (segment table -> per-row / per-key bounds).  With
+// host_table the table is host memory of at most kInlineSeg segments and is
+// passed to the kernel by value; otherwise it is a device copy.
+constexpr int kInlineSeg = 126;
+constexpr int kInlineTableInts = 3 * kInlineSeg + 2;
+hipError_t launch_meta_build(const int32_t* table, bool host_table, int n_seg, int batch, int seq_len,
                              int row_offset, int q_len, int32_t* d_meta, hipStream_t stream);
 
 // Generic kernels: any head_dim <= 256 that is a multiple of 8, f32 or bf16.

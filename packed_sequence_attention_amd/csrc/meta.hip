@@ -24,12 +24,9 @@ __device__ __forceinline__ int upper_index(const int32_t* a, int n, int64_t x) {
   return lo;
 }
 
-__global__ void meta_rows_kernel(const int32_t* __restrict__ table, int n_seg, int batch,
-                                 int seq_len, int row_offset, int q_len, int32_t* __restrict__ row_lo,
-                                 int32_t* __restrict__ row_hi) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t n_rows = static_cast<int64_t>(batch) * q_len;
-  if (idx >= n_rows) return;
+// Row idx (of batch * q_len): the key interval [lo, hi) it attends.
+__device__ __forceinline__ void row_bounds(const int32_t* table, int n_seg, int seq_len, int row_offset,
+                                           int q_len, int64_t idx, int32_t* lo_out, int32_t* hi_out) {
   const int32_t* cu_q = table;
   const int32_t* cu_k = table + n_seg + 1;
   const int32_t* kb = table + 2 * (n_seg + 1);
@@ -51,16 +48,14 @@ __global__ void meta_rows_kernel(const int32_t* __restrict__ table, int n_seg, i
       hi = static_cast<int>(ch);
     }
   }
-  row_lo[idx] = lo;
-  row_hi[idx] = hi;
+  *lo_out = lo;
+  *hi_out = hi;
 }
 
-__global__ void meta_keys_kernel(const int32_t* __restrict__ table, int n_seg, int batch,
-                                 int seq_len, int row_offset, int q_len, int32_t* __restrict__ key_qlo,
-                                 int32_t* __restrict__ key_qhi) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t n_keys = static_cast<int64_t>(batch) * seq_len;
-  if (idx >= n_keys) return;
+// Key idx (of batch * seq_len): the interval [qlo, qhi) of local rows
+// attending it.
+__device__ __forceinline__ void key_bounds(const int32_t* table, int n_seg, int seq_len, int q_len,
+                                           int64_t idx, int32_t* qlo_out, int32_t* qhi_out) {
   const int32_t* cu_q = table;
   const int32_t* cu_k = table + n_seg + 1;
   const int32_t* kb = table + 2 * (n_seg + 1);
@@ -85,33 +80,64 @@ __global__ void meta_keys_kernel(const int32_t* __restrict__ table, int n_seg, i
       if (qlo == qhi) qlo = qhi = 0;
     }
   }
-  key_qlo[idx] = qlo;
-  key_qhi[idx] = qhi;
+  *qlo_out = qlo;
+  *qhi_out = qhi;
+}
+
+// One launch for both halves: threads [0, n_rows) write row bounds, the
+// rest key bounds.
+__device__ __forceinline__ void meta_one(const int32_t* table, int n_seg, int seq_len, int row_offset,
+                                         int q_len, int64_t n_rows, int64_t n_keys, MetaView m) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx < n_rows) {
+    row_bounds(table, n_seg, seq_len, row_offset, q_len, idx, const_cast<int32_t*>(m.row_lo) + idx,
+               const_cast<int32_t*>(m.row_hi) + idx);
+  } else if (idx < n_rows + n_keys) {
+    const int64_t kidx = idx - n_rows;
+    key_bounds(table, n_seg, seq_len, q_len, kidx, const_cast<int32_t*>(m.key_qlo) + kidx,
+               const_cast<int32_t*>(m.key_qhi) + kidx);
+  }
+}
+
+__global__ void meta_kernel(const int32_t* __restrict__ table, int n_seg, int seq_len, int row_offset,
+                            int q_len, int64_t n_rows, int64_t n_keys, MetaView m) {
+  meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
+}
+
+// The table passed by value in the kernel arguments (small tables): no
+// host-to-device copy before the launch.  Each block stages it in LDS.
+struct InlineTable {
+  int32_t v[kInlineTableInts];
+};
+
+__global__ void meta_inline_kernel(InlineTable tab, int n_seg, int seq_len, int row_offset, int q_len,
+                                   int64_t n_rows, int64_t n_keys, MetaView m) {
+  __shared__ int32_t sh[kInlineTableInts];
+  const int n_int = 3 * n_seg + 2;
+  for (int i = threadIdx.x; i < n_int; i += blockDim.x) sh[i] = tab.v[i];
+  __syncthreads();
+  meta_one(sh, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
 }
 
 }  // namespace
 
-hipError_t launch_meta_build(const int32_t* d_table, int n_seg, int batch, int seq_len,
+hipError_t launch_meta_build(const int32_t* table, bool host_table, int n_seg, int batch, int seq_len,
                              int row_offset, int q_len, int32_t* d_meta, hipStream_t stream) {
   MetaView m = meta_view(d_meta, batch, seq_len, q_len);
   const int64_t n_rows = static_cast<int64_t>(batch) * q_len;
   const int64_t n_keys = static_cast<int64_t>(batch) * seq_len;
-  if (n_rows > 0) {
-    dim3 grid(static_cast<unsigned>((n_rows + 255) / 256));
-    meta_rows_kernel<<<grid, 256, 0, stream>>>(d_table, n_seg, batch, seq_len, row_offset, q_len,
-                                               const_cast<int32_t*>(m.row_lo),
-                                               const_cast<int32_t*>(m.row_hi));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  const int64_t n = n_rows + n_keys;
+  if (n == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  if (host_table) {
+    InlineTable tab;
+    const int n_int = 3 * n_seg + 2;
+    for (int i = 0; i < kInlineTableInts; ++i) tab.v[i] = i < n_int ? table[i] : 0;
+    meta_inline_kernel<<<grid, 256, 0, stream>>>(tab, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
+  } else {
+    meta_kernel<<<grid, 256, 0, stream>>>(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
   }
-  if (n_keys > 0) {
-    dim3 grid(static_cast<unsigned>((n_keys + 255) / 256));
-    meta_keys_kernel<<<grid, 256, 0, stream>>>(d_table, n_seg, batch, seq_len, row_offset, q_len,
-                                               const_cast<int32_t*>(m.key_qlo),
-                                               const_cast<int32_t*>(m.key_qhi));
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace bd

@@ -169,6 +169,28 @@ def test_attention_entry_points_reject_before_launch():
     assert lib.blockdiag_meta_ints(2, 100, 40) == 2 * 2 * 40 + 2 * 2 * 100
 
 
+def test_meta_build_host_rejects_before_launch():
+    """The by-value metadata entry point checks its arguments and the table
+    size on the host and launches nothing when they fail."""
+    lib = bd.load_library()
+    N = None
+    mx = lib.blockdiag_meta_inline_max_seg()
+    assert mx >= 64
+    table = np.zeros(3 * (mx + 1) + 2, np.int32)
+    p = 16  # non-null dummy device pointer; never dereferenced because the check fails first
+    # one segment over the limit: capacity error, the caller falls back to the device copy
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), mx + 1, 1, 64, 0, 64, p, N) == 3
+    assert b"segments" in lib.blockdiag_last_error()
+    # empty table for a non-empty chunk; negative sizes; chunk out of range; null pointers
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 0, 1, 64, 0, 64, p, N) == 2
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, -1, 64, 0, 64, p, N) == 1
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, 1, 64, 32, 64, p, N) == 1
+    assert lib.blockdiag_meta_build_host(N, 1, 1, 64, 0, 64, p, N) == 1
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, 1, 64, 0, 64, N, N) == 1
+    # nothing to build is a no-op
+    assert lib.blockdiag_meta_build_host(N, 0, 0, 0, 0, 0, N, N) == 0
+
+
 def test_doc_lens_from_ids():
     assert bd.doc_lens_from_ids([0, 0, 0, 1, 2, 2, -1, -1]) == [3, 1, 2]
     assert bd.doc_lens_from_ids([5, 5, 5, 5]) == [4]

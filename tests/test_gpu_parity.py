@@ -64,6 +64,39 @@ def test_metadata_bit_exact_random_layouts():
             np.testing.assert_array_equal(g_, r_)
 
 
+@gpu
+def test_metadata_inline_and_device_tables_agree():
+    """The table passed by value in the launch arguments and the table copied
+    to the device give the same metadata, bit for bit, at the size limit of
+    the by-value path and on both sides of it, and both match the oracle."""
+    import packed_sequence_attention_amd as bd
+    from oracle import segment as SEG
+    mx = bd.load_library().blockdiag_meta_inline_max_seg()
+    rng = np.random.default_rng(7)
+    layouts = [([[4] * mx], 4 * mx, 0, 4 * mx), ([[4] * mx], 4 * mx, 100, 200),
+               ([[3] * (mx + 1)], 3 * (mx + 1), 0, 3 * (mx + 1))]
+    for _ in range(6):
+        B = int(rng.integers(1, 4)); S = int(rng.integers(64, 600))
+        rows = [[int(x) for x in rng.integers(1, 40, size=int(rng.integers(1, 40)))] for _ in range(B)]
+        rows = [r if sum(r) <= S else [S] for r in rows]
+        a = int(rng.integers(0, S)); b = int(rng.integers(a + 1, S + 1))
+        layouts.append((rows, S, a, b - a))
+    for rows, S, a, L in layouts:
+        _log(f"meta inline/device S={S} chunk=[{a},{a + L}) rows={len(rows)}")
+        t = bd.segment(rows, S, a, L)
+        ref = SEG.mask_bounds_np(rows, S, a, L)
+        dev = [x.cpu().numpy() for x in t.to("cuda", inline=False).meta_views()]
+        for g_, r_ in zip(dev, ref):
+            np.testing.assert_array_equal(g_, r_)
+        if t.n_seg <= mx:
+            inl = [x.cpu().numpy() for x in t.to("cuda", inline=True).meta_views()]
+            for g_, r_ in zip(inl, dev):
+                np.testing.assert_array_equal(g_, r_)
+        else:
+            with pytest.raises(bd.BlockdiagError):
+                t.to("cuda", inline=True)
+
+
 def _rand_docs(seed, S, fill=None, lo=1, hi=None):
     rng = np.random.default_rng(seed)
     fill = S if fill is None else fill
