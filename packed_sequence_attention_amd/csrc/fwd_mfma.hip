@@ -174,6 +174,21 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
   const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
+  // Byte offsets in a V tile of this lane's two transpose reads for block db
+  // (rows tr_row and tr_row + 8 of each 16-row group; the swizzle repeats
+  // every 16 rows, so other groups add a multiple of 16 rows).  Each read's
+  // address is the stage's base plus one integer: the compiler tags an LDS
+  // access with its LDS object only through a few address steps, and an
+  // untagged read is made to wait for every direct load in flight (here the
+  // next tile's, into the other stage) in the middle of the products.
+  int tro[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
+    const int half = (tr_s & 1) * 8;
+    tro[db][0] = tr_row * RP + ((chunk ^ rswz<D>(tr_row)) << 4) + half;
+    tro[db][1] = (tr_row + 8) * RP + ((chunk ^ rswz<D>(tr_row + 8)) << 4) + half;
+  }
 
   if (kmax > kmin) {
     const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
@@ -242,14 +257,10 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
         // O^T += V^T P^T: A = V^T (rows = keys in accumulator order).
 #pragma unroll
         for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
-          const int swa = rswz<D>(ra), swb = rswz<D>(rb);
+          const int r0 = (sb * 32 + 16 * kk2) * RP;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
-            const int half = (tr_s & 1) * 8;
-            const bf16x8 va = lds_tr_pair(sV + ra * RP + ((chunk ^ swa) << 4) + half,
-                                          sV + rb * RP + ((chunk ^ swb) << 4) + half);
+            const bf16x8 va = lds_tr_pair(sV + (tro[db][0] + r0), sV + (tro[db][1] + r0));
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk2], oacc[db], 0, 0, 0);
           }
         }
