@@ -118,71 +118,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   const bool key_ok = key < s.seq_len;
   const int64_t kv_row = (static_cast<int64_t>(b) * s.seq_len + key) * s.h_kv + g;
 
-  // K fragments of this wave's keys (B operand of S) in registers; the
-  // workgroup's V tile (B operand of dP) in LDS, swizzled like Q / dO.
-  bf16x8 kf[KK];
-  char* sV = vt + kgrp * kKW * L::QP;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    if (key_ok) {
-      kf[kk] = *reinterpret_cast<const bf16x8*>(k + kv_row * D + kk * 16 + kg * 8);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) kf[kk][i] = static_cast<__bf16>(0.f);
-    }
-  }
-  if (hsub == 0) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 x;
-      if (key_ok) {
-        x = *reinterpret_cast<const bf16x8*>(v + kv_row * D + kk * 16 + kg * 8);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = static_cast<__bf16>(0.f);
-      }
-      *reinterpret_cast<bf16x8*>(sV + n * L::QP + (((2 * kk + kg) ^ qswz<D>(n)) << 4)) = x;
-    }
-  }
-  // Local rows attending this lane's key: [qlo_k, qhi_k) (empty: qlo_k >= qhi_k).
-  int qlo_k = INT_MAX, qhi_k = INT_MIN;
+  // Local rows attending this lane's key: [a0, a1) when a1 > a0 (loaded
+  // here, used after the other prologue loads have been issued).
+  int a0 = 0, a1 = 0;
   if (key_ok) {
     const int64_t kidx = static_cast<int64_t>(b) * s.seq_len + key;
-    const int a0 = m.key_qlo[kidx], a1 = m.key_qhi[kidx];
-    if (a1 > a0) {
-      qlo_k = a0;
-      qhi_k = a1;
-    }
+    a0 = m.key_qlo[kidx];
+    a1 = m.key_qhi[kidx];
   }
-  const int wqlo = wave_min_i(qlo_k), wqhi = wave_max_i(qhi_k);
-  // Rows inside every key's interval of this wave: [kq_lo_max, kq_hi_min).
-  const int kq_lo_max = wave_max_i(qlo_k), kq_hi_min = wave_min_i(qhi_k);
-  // (Tested per tile as a per-lane compare: a uniform branch there makes the
-  // compiler restructure the loop and run out of registers.)
-  int kq_lo_v = kq_lo_max, kq_hi_v = kq_hi_min;
-  asm volatile("" : "+v"(kq_lo_v), "+v"(kq_hi_v));
-  // Element mask: row t is allowed iff (unsigned)(t - mask_lo) < mask_span.
-  const int mask_lo = qhi_k > qlo_k ? qlo_k : 0;
-  const unsigned mask_span = qhi_k > qlo_k ? static_cast<unsigned>(qhi_k - qlo_k) : 0u;
-  if (lane == 0 && hsub == 0) {
-    sRed[kgrp] = wqlo;
-    sRed[2 + kgrp] = wqhi;
-  }
-  __syncthreads();
-  const int gqlo = min(sRed[0], sRed[1]);
-  const int gqhi = max(sRed[2], sRed[3]);
-
-  f32x16 dkacc[DB], dvacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) dkacc[db][j] = dvacc[db][j] = 0.f;
-
-  const float c = s.scale * kLog2e;
-  // Per-lane LDS addressing.
-  const int tr_row = 4 * kg + ((lane & 15) >> 2);   // transpose-load row within a group of 8
-  const int tr_g = (lane >> 4) & 1;                 // 16-column half of a transpose load
-  const int tr_s = lane & 3;                        // 4-column quarter
   const int row_stride = s.h_q * D;  // elements between consecutive rows
 
   // Q / dO / statistics staging: direct global -> LDS loads (buffer form,
@@ -192,9 +135,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // pair, key group 0 loads Q, key group 1 loads dO and the row statistics.
   // Q / dO land in the swizzled layout: lane l of a load writes LDS chunk
   // (base + l), so each lane fetches the global chunk that belongs there.
-  const int qt0 = gqlo / kQB;
-  const int n_q = gqhi > gqlo ? (gqhi - 1) / kQB - qt0 + 1 : 0;
-  const int n_it = n_q * (s.group / kHW);
   typedef __attribute__((address_space(3))) void lds_void;
   // Per-lane part of the direct-load offsets: load i of a wave covers RPL
   // tile rows (64 lanes x 16 bytes = 4 rows of 16 chunks for head_dim 128,
@@ -203,9 +143,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // common to the wave goes into the resource base.
   constexpr int RPL = 64 / CH;  // rows per direct load
   constexpr int PER = 16 / RPL;
-  auto issue_loads = [&](int it, int buf) {
-    const int h = g * s.group + (it / n_q) * kHW + hsub;
-    const int t0 = (qt0 + it % n_q) * kQB;
+  auto issue_tile = [&](int h, int t0, int buf) {
     // row t0 of (b, h); bytes from there to the end of the tensor's rows for this head
     const int64_t tile0 = ((static_cast<int64_t>(b) * s.q_len + t0) * s.h_q + h) * D;
     const int nbytes = ((s.q_len - t0) * row_stride - h * D) * 2;
@@ -238,6 +176,81 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     }
   };
 
+  // The first query tile is known before the metadata arrives: no row
+  // attends a key after it, so the first local row attending the
+  // workgroup's keys is max(first key - row_offset, 0) whenever any row
+  // attends them.  Its loads go out with the K / V / metadata loads (one
+  // memory round trip for the prologue instead of two); the metadata only
+  // confirms the tile below.
+  const int qt0e = max(kt * kKB - s.row_offset, 0) / kQB;
+  const bool early = qt0e * kQB < s.q_len;
+  if (early) issue_tile(g * s.group + hsub, qt0e * kQB, 0);
+
+  // K fragments of this wave's keys (B operand of S) in registers; the
+  // workgroup's V tile (B operand of dP) in LDS, swizzled like Q / dO.
+  // Loads without branches (keys past the row read the row's last key and
+  // are zeroed where the values are used), so that no load waits for the
+  // ones issued before it.
+  const int64_t kv_row_c = key_ok ? kv_row : (static_cast<int64_t>(b) * s.seq_len + s.seq_len - 1) * s.h_kv + g;
+  bf16x8 kf[KK];
+  char* sV = vt + kgrp * kKW * L::QP;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(k + kv_row_c * D + kk * 16 + kg * 8);
+  if (hsub == 0) {
+    // All of the row's loads first, then the LDS stores (one round trip).
+    bf16x8 x[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) x[kk] = *reinterpret_cast<const bf16x8*>(v + kv_row_c * D + kk * 16 + kg * 8);
+    bf16x8 zero;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zero[i] = static_cast<__bf16>(0.f);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      *reinterpret_cast<bf16x8*>(sV + n * L::QP + (((2 * kk + kg) ^ qswz<D>(n)) << 4)) = key_ok ? x[kk] : zero;
+  }
+  // Local rows attending this lane's key: [qlo_k, qhi_k) (empty: qlo_k >= qhi_k).
+  const int qlo_k = a1 > a0 ? a0 : INT_MAX, qhi_k = a1 > a0 ? a1 : INT_MIN;
+  const int wqlo = wave_min_i(qlo_k), wqhi = wave_max_i(qhi_k);
+  // Rows inside every key's interval of this wave: [kq_lo_max, kq_hi_min).
+  const int kq_lo_max = wave_max_i(qlo_k), kq_hi_min = wave_min_i(qhi_k);
+  // (Tested per tile as a per-lane compare: a uniform branch there makes the
+  // compiler restructure the loop and run out of registers.)
+  int kq_lo_v = kq_lo_max, kq_hi_v = kq_hi_min;
+  asm volatile("" : "+v"(kq_lo_v), "+v"(kq_hi_v));
+  // Element mask: row t is allowed iff (unsigned)(t - mask_lo) < mask_span.
+  const int mask_lo = qhi_k > qlo_k ? qlo_k : 0;
+  const unsigned mask_span = qhi_k > qlo_k ? static_cast<unsigned>(qhi_k - qlo_k) : 0u;
+  if (lane == 0 && hsub == 0) {
+    sRed[kgrp] = wqlo;
+    sRed[2 + kgrp] = wqhi;
+  }
+  __syncthreads();
+  const int gqlo = min(sRed[0], sRed[1]);
+  const int gqhi = max(sRed[2], sRed[3]);
+  if (!key_ok) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kf[kk][i] = static_cast<__bf16>(0.f);
+  }
+  const int qt0 = gqlo / kQB;
+  const int n_q = gqhi > gqlo ? (gqhi - 1) / kQB - qt0 + 1 : 0;
+  const int n_it = n_q * (s.group / kHW);
+  auto issue_loads = [&](int it, int buf) {
+    issue_tile(g * s.group + (it / n_q) * kHW + hsub, (qt0 + it % n_q) * kQB, buf);
+  };
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dkacc[db][j] = dvacc[db][j] = 0.f;
+
+  const float c = s.scale * kLog2e;
+  // Per-lane LDS addressing.
+  const int tr_row = 4 * kg + ((lane & 15) >> 2);   // transpose-load row within a group of 8
+  const int tr_g = (lane >> 4) & 1;                 // 16-column half of a transpose load
+  const int tr_s = lane & 3;                        // 4-column quarter
   // Two barriers per iteration, and the two wave groups run half an
   // iteration apart ("ping-pong"): group A (heads 0, 1 of the four) and
   // group B (heads 2, 3) each put one wave on every SIMD, and while one
@@ -253,9 +266,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // a wave's own H2 orders its group's loads and reads.
   const bool late = hsub >= 2;
   if (n_it > 0) {
-    issue_loads(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // The early tile landed before the barrier above (its fence waits for
+    // every load); it is reloaded only if the metadata disagrees.
+    if (!early || qt0 != qt0e) {
+      issue_loads(0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     if (late) __builtin_amdgcn_s_barrier();
   }
   // The loop is unrolled by two so that the stage is a compile-time
