@@ -94,14 +94,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int t = qt * kBM + n;
   const bool valid = t < s.q_len;
   const int64_t bt = static_cast<int64_t>(b) * s.q_len + t;
-  int lo = 0, hi = 0;
-  float lse2 = 0.f;
   const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
-  if (valid) {
-    lo = m.row_lo[bt];
-    hi = m.row_hi[bt];
-    lse2 = lse[st] * kLog2e;  // -inf on padding rows
+  // Every prologue load is issued before any of them is used, without
+  // branches (rows past the chunk read the chunk's last row and are zeroed
+  // below), so they share one memory round trip.
+  const int tc = valid ? t : s.q_len - 1;
+  const int64_t btc = static_cast<int64_t>(b) * s.q_len + tc;
+  const int64_t stc = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + tc;
+  const int lo_l = m.row_lo[btc], hi_l = m.row_hi[btc];
+  const float lse_l = lse[stc];
+  bf16x8 qf[KK], of[KK], ov[KK];
+  {
+    const int64_t row = (btc * s.h_q + h) * D + kg * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(q + row + kk * 16);
+      of[kk] = *reinterpret_cast<const bf16x8*>(d_o + row + kk * 16);
+      ov[kk] = *reinterpret_cast<const bf16x8*>(o + row + kk * 16);
+    }
   }
+  const int lo = valid ? lo_l : 0, hi = valid ? hi_l : 0;
+  const float lse2 = valid ? lse_l * kLog2e : 0.f;  // -inf on padding rows
   const bool real = hi > lo;
   const int kmin = wave_min_i(real ? lo : INT_MAX);
   const int kmax = wave_max_i(real ? hi : 0);
@@ -109,32 +122,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const bool all_real = wave_min_i(real ? 1 : 0) == 1;
   const int pfirst = s.row_offset + qt * kBM;
 
-  bf16x8 qf[KK], of[KK];
-  {
-    const int64_t row = (bt * s.h_q + h) * D + kg * 8;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (valid) {
-        qf[kk] = *reinterpret_cast<const bf16x8*>(q + row + kk * 16);
-        of[kk] = *reinterpret_cast<const bf16x8*>(d_o + row + kk * 16);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qf[kk][i] = of[kk][i] = static_cast<__bf16>(0.f);
-      }
-    }
-  }
   // Row statistic delta = dO . O (float32): this lane's half of the row, then
   // the partner lane's.  The (lse * log2(e), delta) pair is also written for
   // the dK/dV kernel, which runs after this one.
   float dlt = 0.f;
-  if (valid) {
-    const int64_t row = (bt * s.h_q + h) * D + kg * 8;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(o + row + kk * 16);
+  for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dlt = fmaf(static_cast<float>(of[kk][i]), static_cast<float>(ov[i]), dlt);
-    }
+    for (int i = 0; i < 8; ++i) dlt = fmaf(static_cast<float>(of[kk][i]), static_cast<float>(ov[kk][i]), dlt);
+  if (!valid) {
+    dlt = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[kk][i] = of[kk][i] = static_cast<__bf16>(0.f);
   }
   dlt = pair32_sum(dlt);
   if (valid && kg == 0) *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse2, dlt);

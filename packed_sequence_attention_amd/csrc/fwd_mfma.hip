@@ -105,32 +105,23 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
   const int t = qt * kBM + n;
   const bool valid = t < s.q_len;
   const int64_t bt = static_cast<int64_t>(b) * s.q_len + t;
-  int lo = 0, hi = 0;
-  if (valid) {
-    lo = m.row_lo[bt];
-    hi = m.row_hi[bt];
+  // The metadata and Q loads go out together, without branches (rows past
+  // the chunk read the chunk's last row and are zeroed below).
+  const int64_t btc = static_cast<int64_t>(b) * s.q_len + (valid ? t : s.q_len - 1);
+  const int lo_l = m.row_lo[btc], hi_l = m.row_hi[btc];
+  bf16x8 qf[KK];
+  {
+    const uint16_t* qrow = q + (btc * s.h_q + h) * D + kg * 8;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16);
   }
+  const int lo = valid ? lo_l : 0, hi = valid ? hi_l : 0;
   const bool real = hi > lo;
   const int kmin = wave_min_i(real ? lo : INT_MAX);
   const int kmax = wave_max_i(real ? hi : 0);
   const int lomax = wave_max_i(real ? lo : 0);
   const bool all_real = wave_min_i(real ? 1 : 0) == 1;
   const int pfirst = s.row_offset + qt * kBM;
-
-  bf16x8 qf[KK];
-  {
-    const uint16_t* qrow = q + (bt * s.h_q + h) * D + kg * 8;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (valid) {
-        qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(0.f);
-      }
-    }
-  }
-
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -194,6 +185,12 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
     const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
 #pragma unroll
     for (int cc = 0; cc < 2 * L::NCH; ++cc) issue_chunk(kt0, 0, cc, true);
+    if (!valid) {  // after the tile's loads are issued, so they overlap the Q loads
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(0.f);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Unrolled by two so that the stage is a compile-time constant.
