@@ -14,8 +14,10 @@
 // those rows and keeps its Q and dO rows (B operands), LSE, delta and the
 // dQ^T accumulator in registers.  Key tiles of 64 are streamed through an
 // LDS double buffer with direct global -> LDS loads (buffer form: keys past
-// the row read as zero); only tiles in [doc_start(first row), last row] are
-// visited and the mask is applied only on tiles not entirely allowed.  Per
+// the row read as zero); the tiles from the workgroup's last row down to
+// doc_start(first row) are visited in descending order (the first one is
+// known before the metadata arrives) and the mask is applied only on tiles
+// not entirely allowed.  Per
 // 32-key block (v_mfma_f32_32x32x16_bf16, lane l: query row l % 32):
 //   S^T  = K Q^T    (A = K rows from LDS, B = Q in registers)
 //   dP^T = V dO^T   (A = V rows from LDS, B = dO in registers)
@@ -113,6 +115,55 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       ov[kk] = *reinterpret_cast<const bf16x8*>(o + row + kk * 16);
     }
   }
+  const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
+  const int kv_stride = s.h_kv * D;
+  const int kv_bytes = (s.seq_len * kv_stride - g * D) * 2;
+  // Direct load c (of 2 NCH: K and V chunks alternately) of key tile kt into
+  // stage buf.  The loads of the next tile are spread over the first S/dP
+  // block (one per step): issued together, a workgroup's loads queue up at
+  // the address unit and stall the waves.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // With live == false the load reads nothing (zero-sized resource) and
+  // writes zeros into the free stage: the loop issues it unconditionally, as
+  // a branch around it would split the S/dP block and stop the scheduler
+  // from overlapping its LDS reads with the products.
+  // Per-lane part of the offsets of load i (K and V tiles share it); the
+  // tile's row offset goes into the resource base.
+  int dma_off[L::NCH];
+#pragma unroll
+  for (int i = 0; i < L::NCH; ++i) {
+    const int lc = i * 256 + wave_u * 64 + lane;  // LDS chunk written by this lane
+    const int r = lc / CH, pc = lc % CH;
+    dma_off[i] = (r * kv_stride + (pc ^ rswz<D>(r)) * 8) * 2;
+  }
+  auto issue_chunk = [&](int kt, int buf, int c, bool live) {
+    char* sK = buf == 0 ? stage0 : stage1;
+    char* dst = (c & 1) ? sK + kBN * RP : sK;
+    const int i = c >> 1;
+    const int tile_off = kt * kBN * kv_stride;  // elements
+    const int vo = dma_off[i];
+    const int nbytes = live ? kv_bytes - tile_off * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(((c & 1) ? v : k) + kv0 + tile_off), 0, nbytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16,
+                                             vo, 0, 0, 0);
+  };
+  static_assert(2 * L::NCH == KK, "one direct load per step of the first S/dP block");
+
+  // Key tiles are visited from the last one (the tile's diagonal, known from
+  // its position) down to the first document start, so the first tile's
+  // loads go out with the prologue loads; a row's dQ depends only on the
+  // tiles that are not fully masked for it, summed in descending order
+  // whatever the chunk (fully masked tiles add exact zeros).
+  const int kt1 = (s.row_offset + min(qt * kBM + kBM - 1, s.q_len - 1)) / kBN;
+#pragma unroll
+  for (int c = 0; c < 2 * L::NCH; ++c) issue_chunk(kt1, 0, c, true);
+  // Keep the metadata reductions below these loads, and the Q loads above
+  // them (the compiler would otherwise move each load next to its use).
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[kk]));
+
   const int lo = valid ? lo_l : 0, hi = valid ? hi_l : 0;
   const float lse2 = valid ? lse_l * kLog2e : 0.f;  // -inf on padding rows
   const bool real = hi > lo;
@@ -152,55 +203,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const float lse2m = real ? lse2 : INFINITY;
 
   // Direct loads of key tile kt into buffer buf (keys past the row read 0).
-  const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
-  const int kv_stride = s.h_kv * D;
-  const int kv_bytes = (s.seq_len * kv_stride - g * D) * 2;
-  // Direct load c (of 2 NCH: K and V chunks alternately) of key tile kt into
-  // stage buf.  The loads of the next tile are spread over the first S/dP
-  // block (one per step): issued together, a workgroup's loads queue up at
-  // the address unit and stall the waves.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // With live == false the load reads nothing (zero-sized resource) and
-  // writes zeros into the free stage: the loop issues it unconditionally, as
-  // a branch around it would split the S/dP block and stop the scheduler
-  // from overlapping its LDS reads with the products.
-  // Per-lane part of the offsets of load i (K and V tiles share it); the
-  // tile's row offset goes into the resource base.
-  int dma_off[L::NCH];
-#pragma unroll
-  for (int i = 0; i < L::NCH; ++i) {
-    const int lc = i * 256 + wave_u * 64 + lane;  // LDS chunk written by this lane
-    const int r = lc / CH, pc = lc % CH;
-    dma_off[i] = (r * kv_stride + (pc ^ rswz<D>(r)) * 8) * 2;
-  }
-  auto issue_chunk = [&](int kt, int buf, int c, bool live) {
-    char* sK = buf == 0 ? stage0 : stage1;
-    char* dst = (c & 1) ? sK + kBN * RP : sK;
-    const int i = c >> 1;
-    const int tile_off = kt * kBN * kv_stride;  // elements
-    const int vo = dma_off[i];
-    const int nbytes = live ? kv_bytes - tile_off * 2 : 0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(((c & 1) ? v : k) + kv0 + tile_off), 0, nbytes, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16,
-                                             vo, 0, 0, 0);
-  };
-  static_assert(2 * L::NCH == KK, "one direct load per step of the first S/dP block");
 
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
   const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
 
   if (kmax > kmin) {
-    const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
-#pragma unroll
-    for (int c = 0; c < 2 * L::NCH; ++c) issue_chunk(kt0, 0, c, true);
+    const int kt0 = kmin / kBN;  // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Unrolled by two so that the stage is a compile-time constant.
     auto step = [&](int kt, auto stage) {
       constexpr int buf = decltype(stage)::value;
-      const bool pre = kt < kt1;  // tile kt+1 goes to the other stage, last read before the last barrier
+      const bool pre = kt > kt0;  // tile kt-1 goes to the other stage, last read before the last barrier
       const char* sK = buf == 0 ? stage0 : stage1;
       const char* sV = sK + kBN * RP;
       const int k0 = kt * kBN;
@@ -216,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
           const int pos = rown * RP + (((2 * kk + kg) ^ nat_swz) << 4);
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + pos);
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(sV + pos);
-          if (sb == 0) issue_chunk(kt + 1, buf ^ 1, kk, pre);
+          if (sb == 0) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk, pre);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], pacc, 0, 0, 0);
         }
@@ -261,10 +276,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
       __syncthreads();
     };
-    for (int kt = kt0; kt <= kt1; kt += 2) {
+    for (int kt = kt1; kt >= kt0; kt -= 2) {
       step(kt, Stage<0>{});
-      if (kt + 1 <= kt1) step(kt + 1, Stage<1>{});
+      if (kt - 1 >= kt0) step(kt - 1, Stage<1>{});
     }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);  // the first tile's loads land before the workgroup's LDS is released
   }
 
   // dqacc[db][j] = dQ^T[d = 32db + (j/4)*8 + kg*4 + j%4][row n]

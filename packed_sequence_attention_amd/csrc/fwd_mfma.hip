@@ -11,10 +11,11 @@
 //   query rows); wave w owns query head 4*hg + w for those 32 rows, so all
 //   four waves share every K/V tile staged in LDS (grouped-query reuse) and
 //   have the same live key range.
-//   Key tiles are 32 keys anchored at multiples of 32 in the row; only tiles
-//   in [doc_start(first real row), last real row] are visited (every one of
-//   them holds an allowed pair), and the element mask is applied only on
-//   tiles that are not entirely allowed.
+//   Key tiles are 32 keys anchored at multiples of 32 in the row; the tiles
+//   from the one holding the workgroup's last row down to the one holding
+//   doc_start(first real row) are visited, in descending order (the first
+//   one is known before the metadata arrives), and the element mask is
+//   applied only on tiles that are not entirely allowed.
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16, lane l, n = l % 32,
 // kg = l / 32):
 //   S^T = K Q^T per 32-key block: A = K rows from LDS, B = the wave's Q rows
@@ -115,13 +116,6 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 16);
   }
-  const int lo = valid ? lo_l : 0, hi = valid ? hi_l : 0;
-  const bool real = hi > lo;
-  const int kmin = wave_min_i(real ? lo : INT_MAX);
-  const int kmax = wave_max_i(real ? hi : 0);
-  const int lomax = wave_max_i(real ? lo : 0);
-  const bool all_real = wave_min_i(real ? 1 : 0) == 1;
-  const int pfirst = s.row_offset + qt * kBM;
   f32x16 oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -162,6 +156,28 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
   };
   static_assert(2 * L::NCH <= KK, "at most one direct load per step of the first S block");
 
+  // Key tiles are visited from the last one (the tile's diagonal, known from
+  // its position) down to the first document start, so the first tile's
+  // loads go out with the metadata and Q loads; a row's result depends only
+  // on the tiles that are not fully masked for it, visited in descending
+  // order whatever the chunk (fully masked tiles change nothing).
+  const int kt1 = (s.row_offset + min(qt * kBM + kBM - 1, s.q_len - 1)) / kBN;
+#pragma unroll
+  for (int cc = 0; cc < 2 * L::NCH; ++cc) issue_chunk(kt1, 0, cc, true);
+  // Keep the metadata reductions below these loads, and the Q loads above
+  // them (the compiler would otherwise move each load next to its use).
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[kk]));
+
+  const int lo = valid ? lo_l : 0, hi = valid ? hi_l : 0;
+  const bool real = hi > lo;
+  const int kmin = wave_min_i(real ? lo : INT_MAX);
+  const int kmax = wave_max_i(real ? hi : 0);
+  const int lomax = wave_max_i(real ? lo : 0);
+  const bool all_real = wave_min_i(real ? 1 : 0) == 1;
+  const int pfirst = s.row_offset + qt * kBM;
+
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
   const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
@@ -182,10 +198,8 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
   }
 
   if (kmax > kmin) {
-    const int kt0 = kmin / kBN, kt1 = (kmax - 1) / kBN;
-#pragma unroll
-    for (int cc = 0; cc < 2 * L::NCH; ++cc) issue_chunk(kt0, 0, cc, true);
-    if (!valid) {  // after the tile's loads are issued, so they overlap the Q loads
+    const int kt0 = kmin / kBN;  // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked
+    if (!valid) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
@@ -196,7 +210,7 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
     // Unrolled by two so that the stage is a compile-time constant.
     auto step = [&](int kt, auto stage) {
       constexpr int buf = decltype(stage)::value;
-      const bool pre = kt < kt1;  // tile kt+1 goes to the other stage, last read before the last barrier
+      const bool pre = kt > kt0;  // tile kt-1 goes to the other stage, last read before the last barrier
       const char* sK = buf == 0 ? stage0 : stage1;
       const char* sV = sK + kBN * RP;
       const int k0 = kt * kBN;
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + rown * RP + (((2 * kk + kg) ^ nat_swz) << 4));
-          if (sb == 0 && kk < 2 * L::NCH) issue_chunk(kt + 1, buf ^ 1, kk, pre);
+          if (sb == 0 && kk < 2 * L::NCH) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk, pre);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
         }
         // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
@@ -265,10 +279,12 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
       __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
       __syncthreads();
     };
-    for (int kt = kt0; kt <= kt1; kt += 2) {
+    for (int kt = kt1; kt >= kt0; kt -= 2) {
       step(kt, Stage<0>{});
-      if (kt + 1 <= kt1) step(kt + 1, Stage<1>{});
+      if (kt - 1 >= kt0) step(kt - 1, Stage<1>{});
     }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);  // the first tile's loads land before the workgroup's LDS is released
   }
 
   const float ltot = pair32_sum(lrun);
