@@ -202,8 +202,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   // masked -inf - (-inf) would be NaN).
   const float lse2m = real ? lse2 : INFINITY;
 
-  // Direct loads of key tile kt into buffer buf (keys past the row read 0).
-
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
   const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
