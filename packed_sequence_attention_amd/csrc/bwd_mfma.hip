@@ -25,7 +25,8 @@
 //                                    load, B = P / dS from the accumulators)
 // dK and dV stay in registers until the end; the four heads' partial sums
 // of each key are then added through LDS in a fixed order ((h0 + h2) +
-// (h1 + h3)) and written once (deterministic).  The element mask uses the
+// (h1 + h3)) and written once (deterministic); for head_dim 128 each wave of
+// a key group sums and writes a quarter of the columns.  The element mask uses the
 // per-key row interval [key_qlo, key_qhi); it also zeroes padding rows and
 // rows past the chunk.
 //
@@ -371,65 +372,126 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 
   // Sum the four heads' partials in a fixed order, (h0 + h2) + (h1 + h3),
   // through LDS (the tile buffers are free once every wave has left the
-  // loop).  A wave's partial is stored lane-major, one float4 per lane per
-  // step, so stores and loads are contiguous.
+  // loop), and write dK and dV once.
   __syncthreads();
-  constexpr int P4 = L::part / 16;  // float4 per wave partial
-  auto slot_ptr = [&](int slot_) {  // slots 0, 1 in stage 0; 2, 3 in stage 1
-    return reinterpret_cast<float4*>(slot_ < 2 ? stage0 : stage1) + (slot_ & 1) * P4;
-  };
-  auto put = [&](int slot_) {
-    float4* p = slot_ptr(slot_);
+  if constexpr (DB == kHW) {
+    // head_dim 128: reduce-scatter.  Wave hsub owns d-block hsub (32 of the
+    // 128 columns) of its key group's dK, then of its dV: it stores its other
+    // three blocks for their owners, and sums the owners' copies of its own
+    // block with its registers.  All eight waves work in each phase; a block
+    // is stored lane-major, one float4 per lane per step (contiguous).
+    // Slot (key group, block, writer) is 4 KB: 16 slots per stage.
+    constexpr int SLOT4 = 16 * 64 / 4;  // float4 per slot
+    static_assert(16 * SLOT4 * 16 <= L::stage, "16 reduction slots per stage");
+    auto slot_ptr = [&](int kg_, int db_, int w_) {
+      const int sl = kg_ * 16 + db_ * 4 + w_;
+      return reinterpret_cast<float4*>(sl < 16 ? stage0 : stage1) + (sl & 15) * SLOT4;
+    };
+    auto reduce = [&](f32x16 (&acc)[DB], uint16_t* out, float mul) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) {
+        if (db == hsub) continue;
+        float4* p = slot_ptr(kgrp, db, hsub);
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int f = (db * 4 + jq) * 2;
-        p[f * 64 + lane] = make_float4(dkacc[db][4 * jq], dkacc[db][4 * jq + 1], dkacc[db][4 * jq + 2],
-                                       dkacc[db][4 * jq + 3]);
-        p[(f + 1) * 64 + lane] = make_float4(dvacc[db][4 * jq], dvacc[db][4 * jq + 1],
-                                             dvacc[db][4 * jq + 2], dvacc[db][4 * jq + 3]);
+        for (int jq = 0; jq < 4; ++jq)
+          p[jq * 64 + lane] = make_float4(acc[db][4 * jq], acc[db][4 * jq + 1], acc[db][4 * jq + 2], acc[db][4 * jq + 3]);
       }
-  };
-  auto add = [&](int slot_) {
-    const float4* p = slot_ptr(slot_);
+      __syncthreads();
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) {
+        if (db != hsub) continue;
+        f32x16 part[kHW];
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const int f = (db * 4 + jq) * 2;
-        const float4 x = p[f * 64 + lane], y = p[(f + 1) * 64 + lane];
-        dkacc[db][4 * jq] += x.x; dkacc[db][4 * jq + 1] += x.y;
-        dkacc[db][4 * jq + 2] += x.z; dkacc[db][4 * jq + 3] += x.w;
-        dvacc[db][4 * jq] += y.x; dvacc[db][4 * jq + 1] += y.y;
-        dvacc[db][4 * jq + 2] += y.z; dvacc[db][4 * jq + 3] += y.w;
+        for (int w = 0; w < kHW; ++w) {
+          if (w == db) {
+            part[w] = acc[db];
+          } else {
+            const float4* p = slot_ptr(kgrp, db, w);
+#pragma unroll
+            for (int jq = 0; jq < 4; ++jq) {
+              const float4 x = p[jq * 64 + lane];
+              part[w][4 * jq] = x.x; part[w][4 * jq + 1] = x.y;
+              part[w][4 * jq + 2] = x.z; part[w][4 * jq + 3] = x.w;
+            }
+          }
+        }
+        const f32x16 r = (part[0] + part[2]) + (part[1] + part[3]);
+        // acc[db][j] = X^T[d = 32db + (j/4)*8 + kg*4 + j%4][key n]
+        if (key_ok) {
+          uint16_t* row = out + kv_row * D + kg * 4 + db * 32;
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            uint2 pk;
+            pk.x = pack_bf16x2(r[4 * jq] * mul, r[4 * jq + 1] * mul);
+            pk.y = pack_bf16x2(r[4 * jq + 2] * mul, r[4 * jq + 3] * mul);
+            *reinterpret_cast<uint2*>(row + jq * 8) = pk;
+          }
+        }
       }
-  };
-  if (hsub >= 2) put((hsub - 2) * 2 + kgrp);
-  __syncthreads();
-  if (hsub < 2) add(hsub * 2 + kgrp);
-  __syncthreads();
-  if (hsub == 1) put(kgrp);
-  __syncthreads();
-  if (hsub != 0) return;
-  add(kgrp);
+    };
+    reduce(dkacc, dk, s.scale);
+    __syncthreads();  // every wave has read its dK blocks before the dV blocks overwrite them
+    reduce(dvacc, dv, 1.f);
+  } else {
+    // head_dim 64: the partials of two waves at a time fit the buffers;
+    // two levels, h0 += h2 and h1 += h3, then h0 += h1.
+    constexpr int P4 = L::part / 16;  // float4 per wave partial
+    auto slot_ptr = [&](int slot_) {  // slots 0, 1 in stage 0; 2, 3 in stage 1
+      return reinterpret_cast<float4*>(slot_ < 2 ? stage0 : stage1) + (slot_ & 1) * P4;
+    };
+    auto put = [&](int slot_) {
+      float4* p = slot_ptr(slot_);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const int f = (db * 4 + jq) * 2;
+          p[f * 64 + lane] = make_float4(dkacc[db][4 * jq], dkacc[db][4 * jq + 1], dkacc[db][4 * jq + 2],
+                                         dkacc[db][4 * jq + 3]);
+          p[(f + 1) * 64 + lane] = make_float4(dvacc[db][4 * jq], dvacc[db][4 * jq + 1],
+                                               dvacc[db][4 * jq + 2], dvacc[db][4 * jq + 3]);
+        }
+    };
+    auto add = [&](int slot_) {
+      const float4* p = slot_ptr(slot_);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const int f = (db * 4 + jq) * 2;
+          const float4 x = p[f * 64 + lane], y = p[(f + 1) * 64 + lane];
+          dkacc[db][4 * jq] += x.x; dkacc[db][4 * jq + 1] += x.y;
+          dkacc[db][4 * jq + 2] += x.z; dkacc[db][4 * jq + 3] += x.w;
+          dvacc[db][4 * jq] += y.x; dvacc[db][4 * jq + 1] += y.y;
+          dvacc[db][4 * jq + 2] += y.z; dvacc[db][4 * jq + 3] += y.w;
+        }
+    };
+    if (hsub >= 2) put((hsub - 2) * 2 + kgrp);
+    __syncthreads();
+    if (hsub < 2) add(hsub * 2 + kgrp);
+    __syncthreads();
+    if (hsub == 1) put(kgrp);
+    __syncthreads();
+    if (hsub != 0) return;
+    add(kgrp);
 
-  // dK, dV of this lane's key: dvacc[db][j] = dV^T[d = 32db + (j/4)*8 + kg*4 + j%4][key n]
-  if (key_ok) {
-    uint16_t* dkr = dk + kv_row * D + kg * 4;
-    uint16_t* dvr = dv + kv_row * D + kg * 4;
+    // dvacc[db][j] = dV^T[d = 32db + (j/4)*8 + kg*4 + j%4][key n]
+    if (key_ok) {
+      uint16_t* dkr = dk + kv_row * D + kg * 4;
+      uint16_t* dvr = dv + kv_row * D + kg * 4;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        uint2 a, bb;
-        a.x = pack_bf16x2(dkacc[db][4 * jq] * s.scale, dkacc[db][4 * jq + 1] * s.scale);
-        a.y = pack_bf16x2(dkacc[db][4 * jq + 2] * s.scale, dkacc[db][4 * jq + 3] * s.scale);
-        bb.x = pack_bf16x2(dvacc[db][4 * jq], dvacc[db][4 * jq + 1]);
-        bb.y = pack_bf16x2(dvacc[db][4 * jq + 2], dvacc[db][4 * jq + 3]);
-        *reinterpret_cast<uint2*>(dkr + db * 32 + jq * 8) = a;
-        *reinterpret_cast<uint2*>(dvr + db * 32 + jq * 8) = bb;
-      }
+        for (int jq = 0; jq < 4; ++jq) {
+          uint2 a, bb;
+          a.x = pack_bf16x2(dkacc[db][4 * jq] * s.scale, dkacc[db][4 * jq + 1] * s.scale);
+          a.y = pack_bf16x2(dkacc[db][4 * jq + 2] * s.scale, dkacc[db][4 * jq + 3] * s.scale);
+          bb.x = pack_bf16x2(dvacc[db][4 * jq], dvacc[db][4 * jq + 1]);
+          bb.y = pack_bf16x2(dvacc[db][4 * jq + 2], dvacc[db][4 * jq + 3]);
+          *reinterpret_cast<uint2*>(dkr + db * 32 + jq * 8) = a;
+          *reinterpret_cast<uint2*>(dvr + db * 32 + jq * 8) = bb;
+        }
+    }
   }
 }
 
