@@ -183,6 +183,12 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
  *   scale multiplies q.k (1/sqrt(head_dim) is the usual choice).
  *   Supported: head_dim in {64, 128} for both dtypes, any other head_dim up
  *   to 256 that is a multiple of 8 through the generic kernel; h_q % h_kv = 0.
+ *   The matrix-core kernels take bf16 with head_dim 64 or 128 and h_q/h_kv a
+ *   multiple of 4 when one batch row of K (or V), in bytes, stays below
+ *   2^31 with one tile of slack ((seq_len + 32) * h_kv * head_dim * 2); the
+ *   backward also needs (seq_len + 64) * h_kv * head_dim * 2 and
+ *   (q_len + 32) * h_q * head_dim * 2 below 2^31.  Everything else runs on
+ *   the generic kernels.
  *   bf16 inputs are multiplied on matrix cores with float32 accumulation; the
  *   outputs are rounded to nearest even.  The forward is bitwise
  *   deterministic (no atomics), so a replayed forward equals the original.
@@ -222,8 +228,9 @@ bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
  * blockdiag_mark_main_kernel -- profiling hook.  The next blockdiag_attn_fwd
  * or blockdiag_attn_bwd call made on this thread records start_event on its
  * stream right before launching its main attention kernel and stop_event
- * right after it (the backward's row-statistics and dQ-conversion kernels
- * fall outside the pair), then forgets both.  The events are hipEvent_t
+ * right after it (the backward's main kernel is its dK/dV kernel; the dQ
+ * and row-statistics kernels before it fall outside the pair), then forgets
+ * both.  The events are hipEvent_t
  * handles passed as void*, created and owned by the caller; NULL, NULL
  * clears a pending request.  Lets a caller time the dominant kernel with
  * events on the stream it runs on.  Returns BD_OK, or BD_ERR_INVALID_ARG

@@ -40,6 +40,10 @@ bool use_mfma(bd_dtype dtype, int32_t head_dim, int32_t h_q, int32_t h_kv, float
   return bd::mfma_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f;
 }
 
+bool use_mfma_fwd(bd_dtype dtype, int32_t seq_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
+  return use_mfma(dtype, head_dim, h_q, h_kv, scale) && bd::fwd_mfma_fits(seq_len, h_kv, head_dim);
+}
+
 bool use_mfma_bwd(bd_dtype dtype, int32_t q_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
   return use_mfma(dtype, head_dim, h_q, h_kv, scale) && bd::bwd_mfma_fits(q_len, h_q, head_dim);
 }
@@ -145,8 +149,8 @@ extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t s
                 q, k, v, d_meta, o, lse, nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = use_mfma(dtype, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
-                                                             : bd::launch_fwd_generic(a, s);
+  hipError_t e = use_mfma_fwd(dtype, seq_len, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
+                                                                          : bd::launch_fwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return BD_OK;
 }

@@ -333,6 +333,12 @@ bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv) {
          (h_q / h_kv) % 4 == 0;
 }
 
+bool fwd_mfma_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim) {
+  // a (batch row, K/V head)'s keys, including the last tile's keys past the
+  // row, must be addressable with 31-bit buffer offsets
+  return (seq_len + kBN) * h_kv * head_dim * 2 < (int64_t{1} << 31);
+}
+
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
   return a.head_dim == 64 ? fwd_mfma_t<64>(a, st) : fwd_mfma_t<128>(a, st);
 }
