@@ -7,6 +7,8 @@
   and others (generic path), grouped-query ratios 1..8, chunks at a
   row_offset with straddling documents, padding, empty and all-padding
   chunks, a single document, many tiny documents;
+* a batch row past 31-bit buffer offsets (2^24 tokens, 2 GiB K and V):
+  the generic kernels' 64-bit indexing, checked on the chunk's documents;
 * the five named workloads at full size: 1, 2, 3 and 5 against the full
   oracle; 4 (a 24576-token document) on sampled rows and keys plus
   full-size invariants.
@@ -163,6 +165,41 @@ def test_empty_chunk_and_zero_gradients():
     dq0, dk0, dv0 = bd.attn_bwd(q0, dv["k"], dv["v"], o0, lse0, q0, seg0)
     torch.cuda.synchronize()
     assert o0.numel() == 0 and torch.all(dk0 == 0) and torch.all(dv0 == 0)
+
+
+
+@gpu
+def test_row_past_31_bit_offsets():
+    """Largest sizes: a batch row of 2^24 tokens whose K and V are 2 GiB each
+    (h_kv = 1, head_dim 64), more than 31-bit buffer offsets address, so
+    every kernel takes its 64-bit-indexed generic form.  The chunk is the
+    row's last 256 rows (two documents after one long one); O, LSE and dQ
+    match the oracle on those two documents alone, dK and dV match it on
+    their keys and are exactly zero on the long document's keys."""
+    import torch
+    import packed_sequence_attention_amd as bd
+    S, tail = 1 << 24, [100, 156]
+    n = sum(tail)
+    w_s, t = H.small_case(95, "bf16", [tail], n, 0, n, 4, 1, 64)
+    ref = H.oracle(w_s, t, block_rows=None)
+    _log(f"row of {S} tokens, chunk of the last {n} rows")
+    seg = bd.segment([[S - n] + tail], S, S - n, n, device="cuda")
+    dev = H.to_device(w_s, t)
+    k = torch.zeros((1, S, 1, 64), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    k[:, S - n:] = dev["k"]
+    v[:, S - n:] = dev["v"]
+    o, lse = bd.attn_fwd(dev["q"], k, v, seg, w_s.scale)
+    dq, dk, dv = bd.attn_bwd(dev["q"], k, v, o, lse, dev["do"], seg, w_s.scale)
+    torch.cuda.synchronize()
+    zero_k = bool((dk[:, :S - n] == 0).all().item()) and bool((dv[:, :S - n] == 0).all().item())
+    got = {"o": o, "lse": lse, "dq": dq, "dk": dk[:, S - n:], "dv": dv[:, S - n:]}
+    got = {name: x.double().cpu().numpy() for name, x in got.items()}
+    del k, v, dk, dv
+    torch.cuda.empty_cache()
+    assert zero_k, "dK / dV must be zero at keys no row of the chunk attends"
+    errs = H.check(w_s, got, ref)
+    _log("  errors", {name: f"{e:.3g}" for name, e in errs.items()})
 
 
 FULL_REPORT = {}
