@@ -181,14 +181,14 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
  *   blockdiag_meta_build for the same batch/seq_len/row_offset/q_len; o
  *   (device, dtype) and lse (device, float32) are written in full.
  *   scale multiplies q.k (1/sqrt(head_dim) is the usual choice).
- *   Supported: head_dim in {64, 128} for both dtypes, any other head_dim up
- *   to 256 that is a multiple of 8 through the generic kernel; h_q % h_kv = 0.
- *   The matrix-core kernels take bf16 with head_dim 64 or 128 and h_q/h_kv a
- *   multiple of 4 when one batch row of K (or V), in bytes, stays below
- *   2^31 with one tile of slack ((seq_len + 32) * h_kv * head_dim * 2); the
- *   backward also needs (seq_len + 64) * h_kv * head_dim * 2 and
+ *   Supported: any head_dim up to 256 that is a multiple of 8, float32 or
+ *   bf16, h_q % h_kv = 0.  bf16 with h_q / h_kv a multiple of 4 runs on the
+ *   matrix-core kernels for head_dim 64 and 128 (the forward also 256) when
+ *   one batch row of K (or V), in bytes, stays below 2^31 with one tile of
+ *   slack: (seq_len + 32) * h_kv * head_dim * 2 for the forward; the
+ *   backward needs (seq_len + 64) * h_kv * head_dim * 2 and
  *   (q_len + 32) * h_q * head_dim * 2 below 2^31.  Everything else runs on
- *   the generic kernels.
+ *   the generic kernels (64-bit indexing, float32 arithmetic).
  *   bf16 inputs are multiplied on matrix cores with float32 accumulation; the
  *   outputs are rounded to nearest even.  The forward is bitwise
  *   deterministic (no atomics), so a replayed forward equals the original.

@@ -41,7 +41,8 @@ bool use_mfma(bd_dtype dtype, int32_t head_dim, int32_t h_q, int32_t h_kv, float
 }
 
 bool use_mfma_fwd(bd_dtype dtype, int32_t seq_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
-  return use_mfma(dtype, head_dim, h_q, h_kv, scale) && bd::fwd_mfma_fits(seq_len, h_kv, head_dim);
+  return bd::mfma_fwd_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f &&
+         bd::fwd_mfma_fits(seq_len, h_kv, head_dim);
 }
 
 bool use_mfma_bwd(bd_dtype dtype, int32_t q_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {

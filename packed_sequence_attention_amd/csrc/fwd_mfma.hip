@@ -28,7 +28,8 @@
 // K / V tiles reach LDS by direct global -> LDS loads (buffer form: keys past
 // the row read as zero) into a two-stage buffer; the loads of the next tile
 // are spread over the tile's S products.  32-key tiles keep a workgroup's
-// LDS at 32 KB, so three workgroups (three waves per SIMD) fit on a CU.
+// LDS at 32 KB, so three workgroups (three waves per SIMD) fit on a CU
+// (head_dim 256: 64 KB and two).
 // Rows are stored without padding, the 16-byte chunk c of row r at chunk
 // c ^ f(r), which keeps both the row reads (16 rows, one chunk) and the
 // transpose reads (4 rows x 4 chunks) free of bank conflicts.
@@ -55,12 +56,19 @@ struct FwdLds {
   static constexpr int NCH = kBN * (D / 8) / 256;  // direct loads per thread per tensor
 };
 
-// Chunk swizzle of row r of a K / V tile.
+// Chunk swizzle of row r of a K / V tile.  A bank depends on the chunk index
+// mod 16 only for row pitches of 256 and 512 bytes, so head_dim 256 uses
+// the swizzle of 128 (it permutes the low four bits of the chunk index).
 template <int D>
 __device__ __forceinline__ int rswz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
+
+// Workgroups per CU: three at head_dim 64 / 128 (32 KB of LDS each), two at
+// 256 (64 KB; the O^T accumulators and Q fragments take 192 registers).
+template <int D>
+constexpr int kFwdOcc = D == 256 ? 2 : 3;
 
 template <int B>
 struct Stage {
@@ -75,7 +83,7 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, MetaView m,
                                                           uint16_t* __restrict__ o,
@@ -188,9 +196,12 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
   // access with its LDS object only through a few address steps, and an
   // untagged read is made to wait for every direct load in flight (here the
   // next tile's, into the other stage) in the middle of the products.
-  int tro[DB][2];
+  // Blocks 4..7 (head_dim 256) read 256 bytes further along the same rows:
+  // the swizzle only permutes the low four bits of the chunk index.
+  constexpr int DBT = DB < 4 ? DB : 4;
+  int tro[DBT][2];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < DBT; ++db) {
     const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
     const int half = (tr_s & 1) * 8;
     tro[db][0] = tr_row * RP + ((chunk ^ rswz<D>(tr_row)) << 4) + half;
@@ -271,7 +282,8 @@ __global__ __launch_bounds__(256, 3) void fwd_mfma_kernel(AttnShape s, const uin
           const int r0 = (sb * 32 + 16 * kk2) * RP;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x8 va = lds_tr_pair(sV + (tro[db][0] + r0), sV + (tro[db][1] + r0));
+            const int r1 = r0 + (db >> 2) * 256;
+            const bf16x8 va = lds_tr_pair(sV + (tro[db & 3][0] + r1), sV + (tro[db & 3][1] + r1));
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk2], oacc[db], 0, 0, 0);
           }
         }
@@ -333,6 +345,10 @@ bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv) {
          (h_q / h_kv) % 4 == 0;
 }
 
+bool mfma_fwd_supported(int dtype, int head_dim, int h_q, int h_kv) {
+  return mfma_supported(dtype, head_dim, h_q, h_kv) || (head_dim == 256 && mfma_supported(dtype, 128, h_q, h_kv));
+}
+
 bool fwd_mfma_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim) {
   // a (batch row, K/V head)'s keys, including the last tile's keys past the
   // row, must be addressable with 31-bit buffer offsets
@@ -340,7 +356,12 @@ bool fwd_mfma_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim) {
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
-  return a.head_dim == 64 ? fwd_mfma_t<64>(a, st) : fwd_mfma_t<128>(a, st);
+  switch (a.head_dim) {
+    case 64: return fwd_mfma_t<64>(a, st);
+    case 128: return fwd_mfma_t<128>(a, st);
+    case 256: return fwd_mfma_t<256>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace bd

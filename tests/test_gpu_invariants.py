@@ -60,6 +60,31 @@ def test_chunk_concatenation(cp):
 
 
 @gpu
+def test_chunk_concatenation_head_dim_256():
+    """The head_dim 256 forward keeps the same key-tile anchoring: uneven
+    chunks (bounds not multiples of the 32-row tile) give O, LSE and dQ
+    equal bit for bit to the single full call."""
+    import torch
+    import packed_sequence_attention_amd as bd
+    docs = [_w2_small()[:6]]
+    S = sum(docs[0])
+    w, t = H.small_case(260, "bf16", docs, S, 0, S, 8, 2, 256)
+    d = H.to_device(w, t)
+    full = bd.segment(docs, S, 0, S, device="cuda")
+    o, lse = bd.attn_fwd(d["q"], d["k"], d["v"], full)
+    dq, _, _ = bd.attn_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], full)
+    bounds = [0, S // 3 + 5, (2 * S) // 3 - 7, S]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        seg = bd.segment(docs, S, int(a), int(b - a), device="cuda")
+        qc = d["q"][:, a:b].contiguous(); doc_ = d["do"][:, a:b].contiguous()
+        oc, lc = bd.attn_fwd(qc, d["k"], d["v"], seg)
+        assert torch.equal(oc, o[:, a:b]), "O differs from the full call"
+        assert torch.equal(lc, lse[:, :, a:b]), "LSE differs from the full call"
+        dqc, _, _ = bd.attn_bwd(qc, d["k"], d["v"], oc, lc, doc_, seg)
+        assert torch.equal(dqc, dq[:, a:b]), "dQ differs from the full call"
+
+
+@gpu
 def test_determinism():
     import torch
     import packed_sequence_attention_amd as bd
