@@ -224,14 +224,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
         const int rown = sb * 32 + n;
+        // K / V row reads two k-steps ahead of their products (the
+        // compiler, left alone, keeps one pair in flight and each pair of
+        // products waits for its reads).
+        constexpr int PF = 2;
+        bf16x8 ak[KK], av[KK];
+#pragma unroll
+        for (int kk = 0; kk < PF; ++kk) {
+          const int pos = rown * RP + (((2 * kk + kg) ^ nat_swz) << 4);
+          ak[kk] = *reinterpret_cast<const bf16x8*>(sK + pos);
+          av[kk] = *reinterpret_cast<const bf16x8*>(sV + pos);
+        }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const int pos = rown * RP + (((2 * kk + kg) ^ nat_swz) << 4);
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(sK + pos);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(sV + pos);
+          if (kk + PF < KK) {
+            const int pos = rown * RP + (((2 * (kk + PF) + kg) ^ nat_swz) << 4);
+            ak[kk + PF] = *reinterpret_cast<const bf16x8*>(sK + pos);
+            av[kk + PF] = *reinterpret_cast<const bf16x8*>(sV + pos);
+          }
           if (sb == 0) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk, pre);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[kk], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, of[kk], pacc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], qf[kk], sacc, 0, 0, 0);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk], of[kk], pacc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
         // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
         // The mask is one block over the whole accumulator (S = -inf, so

@@ -246,6 +246,22 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
             if (key < lo || key >= hi) sacc[j] = -INFINITY;
           }
         }
+        // V^T transpose reads of the O^T products, flattened over (k-step,
+        // column block) and issued two ahead of their products, the first two
+        // before the softmax (head_dim 64 / 128; at 256 the registers for
+        // them are not free, and each read directly precedes its product).
+        constexpr int NV = 2 * DB;
+        constexpr int PFV = D <= 128 ? 2 : 0;
+        auto vread = [&](int st_) {
+          const int r1 = (sb * 32 + 16 * (st_ / DB)) * RP + ((st_ % DB) >> 2) * 256;
+          return lds_tr_pair(sV + (tro[(st_ % DB) & 3][0] + r1), sV + (tro[(st_ % DB) & 3][1] + r1));
+        };
+        bf16x8 vq[NV];
+        if constexpr (PFV > 0) {
+#pragma unroll
+          for (int st_ = 0; st_ < PFV; ++st_) vq[st_] = vread(st_);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         float mx = sacc[0];
 #pragma unroll
         for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
@@ -278,14 +294,15 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
         }
         // O^T += V^T P^T: A = V^T (rows = keys in accumulator order).
 #pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const int r0 = (sb * 32 + 16 * kk2) * RP;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int r1 = r0 + (db >> 2) * 256;
-            const bf16x8 va = lds_tr_pair(sV + (tro[db & 3][0] + r1), sV + (tro[db & 3][1] + r1));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kk2], oacc[db], 0, 0, 0);
+        for (int st_ = 0; st_ < NV; ++st_) {
+          if constexpr (PFV > 0) {
+            if (st_ + PFV < NV) vq[st_ + PFV] = vread(st_ + PFV);
+            __builtin_amdgcn_sched_barrier(0);
+          } else {
+            vq[st_] = vread(st_);
           }
+          oacc[st_ % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[st_], pb[st_ / DB], oacc[st_ % DB], 0, 0, 0);
+          if constexpr (PFV > 0) __builtin_amdgcn_sched_barrier(0);
         }
       }
       __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
