@@ -284,6 +284,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     const char* sQ = (buf == 0 ? stage0 : stage1) + hsub * L::head;
     const char* sdO = sQ + kQB * L::QP;
     const float* sStat = reinterpret_cast<const float*>(sdO + kQB * L::QP);  // (lse2, delta) pairs
+    // The K fragments pass through an empty asm here, before the loads of
+    // tile it+1: without it, the compiler's wait bookkeeping still counted
+    // them as pending from their global loads and made every S product of
+    // the first unrolled step wait for one more of the new tile loads.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(kf[kk]));
     if (it + 1 < n_it) issue_loads(it + 1, buf ^ 1);  // that buffer was last read before the last barrier
 
     f32x16 sacc, pacc;
