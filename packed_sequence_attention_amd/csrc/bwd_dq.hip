@@ -259,6 +259,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             if (key < lo || key >= hi) sacc[j] = -INFINITY;
           }
         }
+        // K^T transpose reads of the dQ^T products, flattened over (k-step,
+        // column block) and issued two ahead of their products, the first
+        // two before the exponentials.
+        constexpr int NT = 2 * DB, PFT = 2;
+        auto kread = [&](int st_) {
+          const int kk2 = st_ / DB, db = st_ % DB;
+          const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
+          const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
+          const int half = (tr_s & 1) * 8;
+          return lds_tr_pair(sK + ra * RP + ((chunk ^ rswz<D>(ra)) << 4) + half,
+                             sK + rb * RP + ((chunk ^ rswz<D>(rb)) << 4) + half);
+        };
+        bf16x8 kq[NT];
+#pragma unroll
+        for (int st_ = 0; st_ < PFT; ++st_) kq[st_] = kread(st_);
+        __builtin_amdgcn_sched_barrier(0);
         float dsv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -273,17 +289,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
         // dQ^T += K^T dS^T: A = K^T (rows = keys in accumulator order).
 #pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
-          const int swa = rswz<D>(ra), swb = rswz<D>(rb);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
-            const int half = (tr_s & 1) * 8;
-            const bf16x8 a_k = lds_tr_pair(sK + ra * RP + ((chunk ^ swa) << 4) + half,
-                                           sK + rb * RP + ((chunk ^ swb) << 4) + half);
-            dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_k, dsb[kk2], dqacc[db], 0, 0, 0);
-          }
+        for (int st_ = 0; st_ < NT; ++st_) {
+          if (st_ + PFT < NT) kq[st_ + PFT] = kread(st_ + PFT);
+          __builtin_amdgcn_sched_barrier(0);
+          dqacc[st_ % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[st_], dsb[st_ / DB], dqacc[st_ % DB], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       __builtin_amdgcn_s_waitcnt(0);  // the next tile's direct loads have landed
