@@ -1,9 +1,11 @@
 """Benchmark of the block-diagonal packed attention hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-host segmentation of the document lengths (blockdiag_segment), the pinned
-upload and device metadata build (blockdiag_meta_build), the forward
-(blockdiag_attn_fwd) and the backward (blockdiag_attn_bwd).  Inputs are
+host segmentation of the document lengths (blockdiag_segment), the device
+metadata build (blockdiag_meta_build_host with the table in the launch
+arguments, or a pinned upload and blockdiag_meta_build for tables of more
+than 126 segments), the forward (blockdiag_attn_fwd) and the backward
+(blockdiag_attn_bwd).  Inputs are
 resident in HBM before the timed region starts.
 
 Metric: useful (unmasked-pair) attention TFLOP/s, counting 4*d*H_q FLOP per
@@ -18,7 +20,8 @@ Printed: one JSON line (rank 0), with
                 per allowed pair and query head each; the backward's fifth,
                 dQ, is credited to the dQ kernel and its recomputation of S
                 and dP is not counted) / its mean duration from HIP events
-                recorded around that kernel on its stream, against the bf16
+                recorded around that kernel on its stream in ten of the timed
+                steps (spread over the timed region), against the bf16
                 dense matrix-core peak; `traffic` from the committed rocprofv3
                 counter summary when it was taken on the current kernel
                 source, else null;
@@ -189,9 +192,10 @@ def main():
         del src, dst
 
     # Inside the timed steps only the dominant kernel (dK/dV) is bracketed by
-    # events: every event recorded between two kernels adds a few
-    # microseconds of stream idle time.  The forward kernel is timed in a
-    # separate loop below.
+    # events, and only in every k-th step (ten samples spread over the timed
+    # region): every event recorded between two kernels adds a few
+    # microseconds of stream idle time to its step.  The forward kernel is
+    # timed in a separate loop below.
     def step(marks=None):
         seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device=dev)
         o, lse = bd.attn_fwd(q, k, v, seg, w.scale)
@@ -204,7 +208,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    marks = [[ev.create() for _ in range(2)] for _ in range(args.steps)]
+    mark_every = max(1, args.steps // 10)
+    marks = [[ev.create() for _ in range(2)] if i % mark_every == 0 else None for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -212,6 +217,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    marks = [m for m in marks if m is not None]
     bwd_ms = [ev.elapsed_ms(m[0], m[1]) for m in marks]
     for m in marks:
         for e in m:
@@ -268,7 +274,7 @@ def main():
         "fwd_kernel_tflops": round(flops_fwd / (fwd_avg * 1e-3) / 1e12, 3),
         "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_kernel", "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": traffic, "launches_timed": len(bwd_ms)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, 14 * D)
