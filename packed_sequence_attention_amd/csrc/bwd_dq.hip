@@ -36,19 +36,26 @@
 namespace bd {
 namespace {
 
-constexpr int kBN = 64;  // keys per tile
 constexpr int kBM = 32;  // query rows per workgroup
+// Keys per tile: 64, or 32 at head_dim 256 (two 32 KB stages).
+template <int D>
+constexpr int kBNd = D == 256 ? 32 : 64;
+constexpr int kBNmax = 64;
+// Workgroups per CU: two, or one at head_dim 256 (its dQ^T accumulators, Q
+// and dO fragments alone take 256 registers; one wave per SIMD may use 512).
+template <int D>
+constexpr int kDqOcc = D == 256 ? 1 : 2;
 
 template <int D>
 struct DqLds {
   static constexpr int RP = D * 2;                  // row pitch (bytes), swizzled chunks
-  static constexpr int tile = 2 * kBN * RP;         // K tile then V tile (one stage)
-  static constexpr int NCH = kBN * (D / 8) / 256;   // direct loads per thread per tensor
+  static constexpr int tile = 2 * kBNd<D> * RP;     // K tile then V tile (one stage)
+  static constexpr int NCH = kBNd<D> * (D / 8) / 256;  // direct loads per thread per tensor
 };
 
 template <int D>
 __device__ __forceinline__ int rswz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  if constexpr (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
@@ -65,13 +72,19 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ o,
     const float* __restrict__ lse, float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dq,
     int n_qt, int n_hg) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
+  constexpr int kBN = kBNd<D>;
+  // dQ columns per workgroup (all of them; the split into parts is kept
+  // general).
+  constexpr int CQ = D;
+  constexpr int NCQ = D / CQ;
+  constexpr int DBQ = CQ / 32;
   constexpr int CH = D / 8;
   using L = DqLds<D>;
   constexpr int RP = L::RP;
@@ -86,9 +99,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int n = lane & 31, kg = lane >> 5;
 
   // Longest-first: the last query tiles of a row have the longest key ranges.
+  const int ch = static_cast<int>(blockIdx.x) % NCQ;  // column part of dQ
+  const int bid = static_cast<int>(blockIdx.x) / NCQ;
   const int per_qt = s.batch * n_hg;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
-  const int rem = static_cast<int>(blockIdx.x) % per_qt;
+  const int qt = n_qt - 1 - bid / per_qt;
+  const int rem = bid % per_qt;
   const int b = rem / n_hg, hg = rem % n_hg;
   const int h = hg * 4 + wave;
   const int g = (hg * 4) / s.group;
@@ -148,7 +163,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16,
                                              vo, 0, 0, 0);
   };
-  static_assert(2 * L::NCH == KK, "one direct load per step of the first S/dP block");
+  constexpr int LSTEP = KK / (2 * L::NCH);
+  static_assert(LSTEP * 2 * L::NCH == KK, "direct loads spread evenly over the first S/dP block");
 
   // Key tiles are visited from the last one (the tile's diagonal, known from
   // its position) down to the first document start, so the first tile's
@@ -189,11 +205,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       for (int i = 0; i < 8; ++i) qf[kk][i] = of[kk][i] = static_cast<__bf16>(0.f);
   }
   dlt = pair32_sum(dlt);
-  if (valid && kg == 0) *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse2, dlt);
+  if (valid && kg == 0 && ch == 0) *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse2, dlt);
 
-  f32x16 dqacc[DB];
+  f32x16 dqacc[DBQ];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DBQ; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqacc[db][j] = 0.f;
   const float c = s.scale * kLog2e;
@@ -227,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         // K / V row reads two k-steps ahead of their products (the
         // compiler, left alone, keeps one pair in flight and each pair of
         // products waits for its reads).
-        constexpr int PF = 2;
+        constexpr int PF = D == 256 ? 1 : 2;
         bf16x8 ak[KK], av[KK];
 #pragma unroll
         for (int kk = 0; kk < PF; ++kk) {
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             ak[kk + PF] = *reinterpret_cast<const bf16x8*>(sK + pos);
             av[kk + PF] = *reinterpret_cast<const bf16x8*>(sV + pos);
           }
-          if (sb == 0) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk, pre);
+          if (sb == 0 && kk % LSTEP == 0) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk / LSTEP, pre);
           __builtin_amdgcn_sched_barrier(0);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], qf[kk], sacc, 0, 0, 0);
           pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk], of[kk], pacc, 0, 0, 0);
@@ -262,9 +278,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         // K^T transpose reads of the dQ^T products, flattened over (k-step,
         // column block) and issued two ahead of their products, the first
         // two before the exponentials.
-        constexpr int NT = 2 * DB, PFT = 2;
+        constexpr int NT = 2 * DBQ, PFT = D == 256 ? 1 : 2;
         auto kread = [&](int st_) {
-          const int kk2 = st_ / DB, db = st_ % DB;
+          const int kk2 = st_ / DBQ, db = ch * DBQ + st_ % DBQ;  // column block of K^T
           const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
           const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
           const int half = (tr_s & 1) * 8;
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         for (int st_ = 0; st_ < NT; ++st_) {
           if (st_ + PFT < NT) kq[st_ + PFT] = kread(st_ + PFT);
           __builtin_amdgcn_sched_barrier(0);
-          dqacc[st_ % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[st_], dsb[st_ / DB], dqacc[st_ % DB], 0, 0, 0);
+          dqacc[st_ % DBQ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[st_], dsb[st_ / DBQ], dqacc[st_ % DBQ], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -307,11 +323,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __builtin_amdgcn_s_waitcnt(0);  // the first tile's loads land before the workgroup's LDS is released
   }
 
-  // dqacc[db][j] = dQ^T[d = 32db + (j/4)*8 + kg*4 + j%4][row n]
+  // dqacc[db][j] = dQ^T[d = ch*CQ + 32db + (j/4)*8 + kg*4 + j%4][row n]
   if (valid) {
-    uint16_t* drow = dq + (bt * s.h_q + h) * D + kg * 4;
+    uint16_t* drow = dq + (bt * s.h_q + h) * D + ch * CQ + kg * 4;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBQ; ++db)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         uint2 pk;
@@ -343,11 +359,16 @@ hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
 bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim) {
   // a (batch row, K/V head)'s keys, including the last tile's keys past the
   // row, must be addressable with 31-bit buffer offsets
-  return (seq_len + kBN) * h_kv * head_dim * 2 < (int64_t{1} << 31);
+  return (seq_len + kBNmax) * h_kv * head_dim * 2 < (int64_t{1} << 31);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
-  return a.head_dim == 64 ? bwd_dq_t<64>(a, st) : bwd_dq_t<128>(a, st);
+  switch (a.head_dim) {
+    case 64: return bwd_dq_t<64>(a, st);
+    case 128: return bwd_dq_t<128>(a, st);
+    case 256: return bwd_dq_t<256>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace bd

@@ -537,7 +537,16 @@ bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim) {
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
-  return a.head_dim == 64 ? bwd_mfma_t<64>(a, st) : bwd_mfma_t<128>(a, st);
+  switch (a.head_dim) {
+    case 64: return bwd_mfma_t<64>(a, st);
+    case 128: return bwd_mfma_t<128>(a, st);
+    case 256: {
+      // The dQ kernel runs first: it also writes the row statistics.
+      const hipError_t e = launch_bwd_dq(a, st);
+      return e != hipSuccess ? e : launch_bwd_dkdv256(a, st);
+    }
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace bd

@@ -54,9 +54,9 @@ hipError_t launch_meta_build(const int32_t* table, bool host_table, int n_seg, i
 hipError_t launch_fwd_generic(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t stream);
 
-// bf16 matrix-core kernels: head_dim in {64, 128}, h_q / h_kv a multiple of 4.
+// bf16 matrix-core kernels: head_dim in {64, 128}, h_q / h_kv a multiple of 4;
 bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv);
-// The forward also takes head_dim 256 on matrix cores (the backward does not).
+// head_dim 256 as well (forward, dQ and the head_dim-256 dK/dV kernel).
 bool mfma_fwd_supported(int dtype, int head_dim, int h_q, int h_kv);
 // The matrix-core forward addresses a (batch row, K/V head)'s keys with
 // 31-bit buffer offsets; larger rows take the generic kernel.
@@ -69,6 +69,9 @@ bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim);
 bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim);
 // dQ of the matrix-core backward (query-stationary); also writes rowstat.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+// dK / dV of the matrix-core backward at head_dim 256 (bwd_dkdv256.hip);
+// reads rowstat.
+hipError_t launch_bwd_dkdv256(const BwdArgs& a, hipStream_t stream);
 
 // Backward row statistics: rowstat = (lse * log2(e), delta = rowsum(dO * O)),
 // float32.
