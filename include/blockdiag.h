@@ -183,7 +183,7 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
  *   scale multiplies q.k (1/sqrt(head_dim) is the usual choice).
  *   Supported: any head_dim up to 256 that is a multiple of 8, float32 or
  *   bf16, h_q % h_kv = 0.  bf16 with h_q / h_kv a multiple of 4 runs on the
- *   matrix-core kernels for head_dim 64 and 128 (the forward also 256) when
+ *   matrix-core kernels for head_dim 64, 128 and 256 when
  *   one batch row of K (or V), in bytes, stays below 2^31 with one tile of
  *   slack: (seq_len + 32) * h_kv * head_dim * 2 for the forward; the
  *   backward needs (seq_len + 64) * h_kv * head_dim * 2 and

@@ -56,7 +56,8 @@ hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t stream);
 
 // bf16 matrix-core kernels: head_dim in {64, 128}, h_q / h_kv a multiple of 4;
 bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv);
-// head_dim 256 as well (forward, dQ and the head_dim-256 dK/dV kernel).
+// the same with head_dim 256 as well (forward, dQ and the head_dim-256 dK/dV
+// kernel).
 bool mfma_fwd_supported(int dtype, int head_dim, int h_q, int h_kv);
 // The matrix-core forward addresses a (batch row, K/V head)'s keys with
 // 31-bit buffer offsets; larger rows take the generic kernel.
