@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default 2)")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="run the named workload's packing and head counts at this head_dim instead "
+                         "(e.g. 256); not the headline configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 launches): a known-size "
@@ -172,6 +175,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synthetic.workload(args.workload)
+    if args.head_dim is not None and args.head_dim != w.head_dim:
+        w = synthetic.custom_workload(w.wid, w.dtype, w.doc_lens, w.seq_len, w.row_offset, w.q_len, w.h_q,
+                                      w.h_kv, args.head_dim,
+                                      name=w.name.replace(f"/{w.head_dim}", f"/{args.head_dim}"))
     t = synthetic.draw_tensors(w)
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     d = {k: torch.from_numpy(v).to(dev, dt) for k, v in t.items()}
@@ -250,7 +257,10 @@ def main():
     value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
     flops_dkdv = 8 * D * Hq * pairs
     achieved = flops_dkdv / (bwd_avg * 1e-3) / 1e12
-    traffic = traffic_from_profile("bwd_dkdv", "bwd_mfma.hip", f"w{args.workload}") if w.dtype == "bf16" else None
+    dkdv_kernel = "bwd_dkdv256_kernel" if D == 256 else "bwd_dkdv_kernel"
+    named = args.head_dim is None or args.head_dim == synthetic.workload(args.workload).head_dim
+    traffic = (traffic_from_profile("bwd_dkdv", "bwd_mfma.hip", f"w{args.workload}")
+               if w.dtype == "bf16" and named else None)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -272,7 +282,7 @@ def main():
         "tflops_fwd_plus_bwd_calls": round((flops_fwd + flops_bwd) / ((tf + tb) * 1e-3) / 1e12, 3),
         "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd_dkdv": round(bwd_avg, 4)},
         "fwd_kernel_tflops": round(flops_fwd / (fwd_avg * 1e-3) / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": "bwd_dkdv_kernel", "achieved": round(achieved, 3),
+        "roofline": {"bound": "mfma", "kernel": dkdv_kernel, "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "launches_timed": len(bwd_ms)},
     }

@@ -61,7 +61,7 @@ def test_chunk_concatenation(cp):
 
 @gpu
 def test_chunk_concatenation_head_dim_256():
-    """The head_dim 256 forward keeps the same key-tile anchoring: uneven
+    """The head_dim 256 kernels keep the same key-tile anchoring: uneven
     chunks (bounds not multiples of the 32-row tile) give O, LSE and dQ
     equal bit for bit to the single full call."""
     import torch

@@ -127,8 +127,8 @@ SMALL = [
     ("bf16", [[70], [300], [129, 1]], 300, 64, 129, 8, 2, 64),
     ("bf16", [[1000]], 1000, 967, 33, 4, 1, 128),
     ("f32", [_rand_docs(11, 380, fill=350)], 380, 0, 380, 4, 1, 64),
-    # head_dim 256 (matrix-core forward, generic backward) and GQA 8:1,
-    # padding tail; float32 head_dim 256 on the generic kernels
+    # head_dim 256 (matrix-core forward and backward) and GQA 8:1, padding
+    # tail; float32 head_dim 256 on the generic kernels
     ("bf16", [_rand_docs(12, 300, fill=280)], 300, 20, 250, 8, 1, 256),
     ("f32", [_rand_docs(13, 200)], 200, 0, 200, 2, 2, 256),
     ("bf16", [_rand_docs(14, 700, hi=400)], 700, 0, 700, 8, 2, 256),
