@@ -12,13 +12,13 @@
 // Work decomposition mirrors the forward: a workgroup is (batch row, 4 query
 // heads sharing one K/V head, 32 local rows); wave w owns head 4*hg + w for
 // those rows and keeps its Q and dO rows (B operands), LSE, delta and the
-// dQ^T accumulator in registers.  Key tiles of 64 are streamed through an
-// LDS double buffer with direct global -> LDS loads (buffer form: keys past
-// the row read as zero); the tiles from the workgroup's last row down to
-// doc_start(first row) are visited in descending order (the first one is
-// known before the metadata arrives) and the mask is applied only on tiles
-// not entirely allowed.  Per
-// 32-key block (v_mfma_f32_32x32x16_bf16, lane l: query row l % 32):
+// dQ^T accumulator in registers (at head_dim 256 these take 256 registers:
+// one workgroup per CU, one wave per SIMD).  Key tiles of 64 (32 at head_dim
+// 256) are streamed through an LDS double buffer with direct global -> LDS
+// loads (buffer form: keys past the row read as zero); the tiles from the
+// workgroup's last row down to doc_start(first row) are visited in
+// descending order (the first one is known before the metadata arrives) and
+// the mask is applied only on tiles not entirely allowed.  Per 32-key block (v_mfma_f32_32x32x16_bf16, lane l: query row l % 32):
 //   S^T  = K Q^T    (A = K rows from LDS, B = Q in registers)
 //   dP^T = V dO^T   (A = V rows from LDS, B = dO in registers)
 //   dS^T = P^T (dP^T - delta) in the accumulator layout, rounded to bf16
@@ -80,11 +80,6 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int kBN = kBNd<D>;
-  // dQ columns per workgroup (all of them; the split into parts is kept
-  // general).
-  constexpr int CQ = D;
-  constexpr int NCQ = D / CQ;
-  constexpr int DBQ = CQ / 32;
   constexpr int CH = D / 8;
   using L = DqLds<D>;
   constexpr int RP = L::RP;
@@ -99,11 +94,9 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   const int n = lane & 31, kg = lane >> 5;
 
   // Longest-first: the last query tiles of a row have the longest key ranges.
-  const int ch = static_cast<int>(blockIdx.x) % NCQ;  // column part of dQ
-  const int bid = static_cast<int>(blockIdx.x) / NCQ;
   const int per_qt = s.batch * n_hg;
-  const int qt = n_qt - 1 - bid / per_qt;
-  const int rem = bid % per_qt;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+  const int rem = static_cast<int>(blockIdx.x) % per_qt;
   const int b = rem / n_hg, hg = rem % n_hg;
   const int h = hg * 4 + wave;
   const int g = (hg * 4) / s.group;
@@ -205,11 +198,11 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
       for (int i = 0; i < 8; ++i) qf[kk][i] = of[kk][i] = static_cast<__bf16>(0.f);
   }
   dlt = pair32_sum(dlt);
-  if (valid && kg == 0 && ch == 0) *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse2, dlt);
+  if (valid && kg == 0) *reinterpret_cast<float2*>(rowstat + 2 * st) = make_float2(lse2, dlt);
 
-  f32x16 dqacc[DBQ];
+  f32x16 dqacc[DB];
 #pragma unroll
-  for (int db = 0; db < DBQ; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqacc[db][j] = 0.f;
   const float c = s.scale * kLog2e;
@@ -278,9 +271,9 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
         // K^T transpose reads of the dQ^T products, flattened over (k-step,
         // column block) and issued two ahead of their products, the first
         // two before the exponentials.
-        constexpr int NT = 2 * DBQ, PFT = D == 256 ? 1 : 2;
+        constexpr int NT = 2 * DB, PFT = D == 256 ? 1 : 2;
         auto kread = [&](int st_) {
-          const int kk2 = st_ / DBQ, db = ch * DBQ + st_ % DBQ;  // column block of K^T
+          const int kk2 = st_ / DB, db = st_ % DB;
           const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
           const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
           const int half = (tr_s & 1) * 8;
@@ -308,7 +301,7 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
         for (int st_ = 0; st_ < NT; ++st_) {
           if (st_ + PFT < NT) kq[st_ + PFT] = kread(st_ + PFT);
           __builtin_amdgcn_sched_barrier(0);
-          dqacc[st_ % DBQ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[st_], dsb[st_ / DBQ], dqacc[st_ % DBQ], 0, 0, 0);
+          dqacc[st_ % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[st_], dsb[st_ / DB], dqacc[st_ % DB], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -323,11 +316,11 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
     __builtin_amdgcn_s_waitcnt(0);  // the first tile's loads land before the workgroup's LDS is released
   }
 
-  // dqacc[db][j] = dQ^T[d = ch*CQ + 32db + (j/4)*8 + kg*4 + j%4][row n]
+  // dqacc[db][j] = dQ^T[d = 32db + (j/4)*8 + kg*4 + j%4][row n]
   if (valid) {
-    uint16_t* drow = dq + (bt * s.h_q + h) * D + ch * CQ + kg * 4;
+    uint16_t* drow = dq + (bt * s.h_q + h) * D + kg * 4;
 #pragma unroll
-    for (int db = 0; db < DBQ; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         uint2 pk;
