@@ -22,7 +22,9 @@ Printed: one JSON line (rank 0), with
                 and dP is not counted) / its mean duration from HIP events
                 recorded around that kernel on its stream in ten of the timed
                 steps (spread over the timed region), against the bf16
-                dense matrix-core peak; `traffic` from the committed rocprofv3
+                dense matrix-core peak (the fp32 vector-ALU peak, bound "alu",
+                for shapes on the generic kernels, e.g. the float32
+                workload 1); `traffic` from the committed rocprofv3
                 counter summary when it was taken on the current kernel
                 source, else null;
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
@@ -43,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
+PEAK_FP32_VALU_TFLOPS = 157.3  # 256 CU x 4 SIMD x 64 fp32 FLOP/clk x 2.4 GHz (vector ALU)
 PEAK_HBM_GBS = 8000.0
 METRIC = "unmasked-pair attention TFLOP/s fwd+bwd (bf16, packed S=4k) and % MFMA peak"
 
@@ -257,10 +260,17 @@ def main():
     value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
     flops_dkdv = 8 * D * Hq * pairs
     achieved = flops_dkdv / (bwd_avg * 1e-3) / 1e12
-    dkdv_kernel = "bwd_dkdv256_kernel" if D == 256 else "bwd_dkdv_kernel"
+    # The kernel the events bracketed: a matrix-core dK/dV kernel (bf16,
+    # head_dim 64 / 128 / 256, GQA ratio a multiple of 4), else the generic
+    # vector-ALU kernel, priced against the fp32 vector peak.
+    on_mfma = w.dtype == "bf16" and D in (64, 128, 256) and (w.h_q // w.h_kv) % 4 == 0
+    if on_mfma:
+        dkdv_kernel, bound, peak = ("bwd_dkdv256_kernel" if D == 256 else "bwd_dkdv_kernel"), "mfma", PEAK_BF16_TFLOPS
+    else:
+        dkdv_kernel, bound, peak = "dkv_generic_kernel", "alu", PEAK_FP32_VALU_TFLOPS
     named = args.head_dim is None or args.head_dim == synthetic.workload(args.workload).head_dim
     traffic = (traffic_from_profile("bwd_dkdv", "bwd_mfma.hip", f"w{args.workload}")
-               if w.dtype == "bf16" and named else None)
+               if on_mfma and D != 256 and named else None)
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -282,8 +292,8 @@ def main():
         "tflops_fwd_plus_bwd_calls": round((flops_fwd + flops_bwd) / ((tf + tb) * 1e-3) / 1e12, 3),
         "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd_dkdv": round(bwd_avg, 4)},
         "fwd_kernel_tflops": round(flops_fwd / (fwd_avg * 1e-3) / 1e12, 3),
-        "roofline": {"bound": "mfma", "kernel": dkdv_kernel, "achieved": round(achieved, 3),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": bound, "kernel": dkdv_kernel, "achieved": round(achieved, 3),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic, "launches_timed": len(bwd_ms)},
     }
     if not args.no_cpu_baseline:
