@@ -24,9 +24,19 @@ Printed: one JSON line (rank 0), with
                 steps (spread over the timed region), against the bf16
                 dense matrix-core peak (the fp32 vector-ALU peak, bound "alu",
                 for shapes on the generic kernels, e.g. the float32
-                workload 1); `traffic` from the committed rocprofv3
+                workload 1); where that kernel's FLOP per algorithmic byte
+                is below the machine balance (short documents, e.g. the
+                fragmented S=49152 workload) it is priced in GB/s against the
+                8 TB/s HBM peak instead (bound "hbm"); `traffic` from the committed rocprofv3
                 counter summary when it was taken on the current kernel
                 source, else null;
+  hbm           algorithmic bytes of the forward and backward entry points
+                (each tensor touched once) and the HBM rate they imply;
+  roofs_us      one step's lower bounds from the matrix-core, HBM and exp
+                roofs next to the measured step;
+  flushed       (--flush-mib) the step timed with a buffer written before
+                each one, so inputs come from HBM rather than L2 / the
+                Infinity Cache;
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
                 sample of the same workload.
 """
@@ -47,6 +57,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk x 2.4 GHz
 PEAK_FP32_VALU_TFLOPS = 157.3  # 256 CU x 4 SIMD x 64 fp32 FLOP/clk x 2.4 GHz (vector ALU)
 PEAK_HBM_GBS = 8000.0
+# exp throughput: v_exp_f32 issues at quarter rate (8 clk per wave64
+# instruction per SIMD, measured) -> 8 exp/clk/SIMD x 1024 SIMDs x 2.4 GHz
+PEAK_EXP_PER_S = 1024 * 8 * 2.4e9
 METRIC = "unmasked-pair attention TFLOP/s fwd+bwd (bf16, packed S=4k) and % MFMA peak"
 
 
@@ -157,6 +170,9 @@ def main():
                     help="run the named workload's packing and head counts at this head_dim instead "
                          "(e.g. 256); not the headline configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="also time steps with a buffer of this many MiB written before each one "
+                         "(evicts Q/K/V/dO from L2 and the Infinity Cache; e.g. 512)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (3 launches): a known-size "
                          "reference for HBM traffic counters")
@@ -191,6 +207,14 @@ def main():
     D, Hq = w.head_dim, w.h_q
     flops_fwd = 4 * D * Hq * pairs
     flops_bwd = 10 * D * Hq * pairs
+    # Algorithmic HBM bytes (every tensor touched once): W = keys in the
+    # chunk's windows, summed over batch rows (the table's total key length).
+    e_sz = 4 if w.dtype == "f32" else 2
+    rows = w.batch * w.q_len
+    win = int(seg0.cu_k[seg0.n_seg])
+    bytes_fwd = 2 * e_sz * D * Hq * rows + 2 * e_sz * D * w.h_kv * win + 4 * Hq * rows
+    bytes_bwd = 4 * e_sz * D * Hq * rows + 4 * e_sz * D * w.h_kv * win + 8 * Hq * rows
+    exps = 2 * Hq * pairs  # one exp per allowed pair and query head, forward and backward
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev)
     if args.copy_mib > 0:
@@ -257,6 +281,26 @@ def main():
     tb = float(np.median(times_b))
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
 
+    flushed = None
+    if args.flush_mib > 0:
+        buf = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        ef = [ev.create() for _ in range(2)]
+        times = []
+        for i in range(max(5, args.steps // 2)):
+            buf.fill_(float(i))
+            ev.record(ef[0], stream)
+            step()
+            ev.record(ef[1], stream)
+            torch.cuda.synchronize()
+            times.append(ev.elapsed_ms(ef[0], ef[1]))
+        for x in ef:
+            ev.destroy(x)
+        del buf
+        tfl = float(np.median(times))
+        flushed = {"flush_mib": args.flush_mib, "ms_per_step": round(tfl, 4),
+                   "tflops": round((flops_fwd + flops_bwd) / (tfl * 1e-3) / 1e12, 3),
+                   "hbm_gbs": round((bytes_fwd + bytes_bwd) / (tfl * 1e-3) / 1e9, 1)}
+
     value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
     flops_dkdv = 8 * D * Hq * pairs
     achieved = flops_dkdv / (bwd_avg * 1e-3) / 1e12
@@ -268,8 +312,17 @@ def main():
         dkdv_kernel, bound, peak = ("bwd_dkdv256_kernel" if D == 256 else "bwd_dkdv_kernel"), "mfma", PEAK_BF16_TFLOPS
     else:
         dkdv_kernel, bound, peak = "dkv_generic_kernel", "alu", PEAK_FP32_VALU_TFLOPS
+    # The dK/dV kernel's algorithmic bytes: Q, dO and the row statistics read
+    # once, K, V read and dK, dV written once over the windows.  Below the
+    # machine balance (peak FLOP/s over 8 TB/s) the kernel is priced against
+    # HBM instead (short documents: few pairs per byte).
+    bytes_dkdv = 2 * e_sz * D * Hq * rows + 4 * e_sz * D * w.h_kv * win + 8 * Hq * rows
+    unit = "TFLOP/s"
+    if flops_dkdv / bytes_dkdv < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
+        achieved = bytes_dkdv / (bwd_avg * 1e-3) / 1e9
     named = args.head_dim is None or args.head_dim == synthetic.workload(args.workload).head_dim
-    traffic = (traffic_from_profile("bwd_dkdv", "bwd_mfma.hip", f"w{args.workload}")
+    traffic = (traffic_from_profile("bwd_dkdv", "bwd_dkdv.h", f"w{args.workload}")
                if on_mfma and D != 256 and named else None)
     out = {
         "metric": METRIC,
@@ -292,10 +345,27 @@ def main():
         "tflops_fwd_plus_bwd_calls": round((flops_fwd + flops_bwd) / ((tf + tb) * 1e-3) / 1e12, 3),
         "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd_dkdv": round(bwd_avg, 4)},
         "fwd_kernel_tflops": round(flops_fwd / (fwd_avg * 1e-3) / 1e12, 3),
+        # Algorithmic HBM bytes of each entry point and the rate they imply at
+        # the entry points' event times, against the 8 TB/s HBM peak.
+        "hbm": {"bytes_fwd": bytes_fwd, "bytes_bwd": bytes_bwd,
+                "gbs_fwd": round(bytes_fwd / (tf * 1e-3) / 1e9, 1),
+                "gbs_bwd": round(bytes_bwd / (tb * 1e-3) / 1e9, 1),
+                "frac_fwd": round(bytes_fwd / (tf * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "frac_bwd": round(bytes_bwd / (tb * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        # Lower bounds on one step's time from each roof (us): useful FLOP at
+        # the bf16 matrix-core peak, algorithmic bytes at 8 TB/s, one exp per
+        # allowed pair and head per direction at the exp rate.
+        "roofs_us": {"mfma": round((flops_fwd + flops_bwd) / (PEAK_BF16_TFLOPS * 1e12) * 1e6, 2),
+                     "hbm": round((bytes_fwd + bytes_bwd) / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
+                     "exp": round(exps / PEAK_EXP_PER_S * 1e6, 2),
+                     "step": round(ms_per_step * 1e3, 2)},
         "roofline": {"bound": bound, "kernel": dkdv_kernel, "achieved": round(achieved, 3),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "algorithmic_flop": flops_dkdv, "algorithmic_bytes": bytes_dkdv,
                      "traffic": traffic, "launches_timed": len(bwd_ms)},
     }
+    if flushed is not None:
+        out["flushed"] = flushed
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, 14 * D)
     print(json.dumps(out), flush=True)

@@ -28,8 +28,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 # register file per instruction makes it split the dK/dV accumulators between
 # AGPRs and VGPRs and copy them every iteration, so that file uses the VGPR
 # form of the MFMA instructions (AGPRs then only hold spilled values).
+# The head_dim 64 instantiation of that kernel is also built with the
+# max-ILP scheduler (measured faster there, slower at head_dim 128).
 EXTRA = {
     "bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd_dkdv64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 

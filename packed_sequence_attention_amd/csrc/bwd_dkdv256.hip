@@ -3,7 +3,7 @@
 //
 // Automodel page "feat(distributed): block-diagonal varlen CP for packed
 // sequences", Proof section (forward/backward parity, input gradients).  The
-// same products as the head_dim 64 / 128 kernel (bwd_mfma.hip):
+// same products as the head_dim 64 / 128 kernel (bwd_dkdv.h):
 //   P_ij = exp(scale q_i.k_j - LSE_i), dP_ij = dO_i . v_j,
 //   dS_ij = P_ij (dP_ij - delta_i),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i.

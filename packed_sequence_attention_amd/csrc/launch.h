@@ -70,9 +70,10 @@ bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim);
 bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim);
 // dQ of the matrix-core backward (query-stationary); also writes rowstat.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
-// dK / dV of the matrix-core backward at head_dim 256 (bwd_dkdv256.hip);
-// reads rowstat.
+// dK / dV of the matrix-core backward at head_dim 256 (bwd_dkdv256.hip) and
+// 64 (bwd_dkdv64.hip); read rowstat.
 hipError_t launch_bwd_dkdv256(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv64(const BwdArgs& a, hipStream_t stream);
 
 // Backward row statistics: rowstat = (lse * log2(e), delta = rowsum(dO * O)),
 // float32.
