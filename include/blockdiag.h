@@ -124,7 +124,8 @@ bd_status blockdiag_validate(const int32_t *cu_seqlens_q, const int32_t *cu_seql
 
 /*
  * blockdiag_meta_ints -- number of int32 in the device metadata buffer that
- * blockdiag_meta_build fills: 2 * batch * q_len + 2 * batch * seq_len.
+ * blockdiag_meta_build fills: 2 * batch * q_len + 2 * batch * seq_len,
+ * plus nq + 2 with nq = batch * ceil(q_len / 32) when 1 <= nq <= 8192.
  *
  * blockdiag_meta_build -- expands a validated segment table (device copy)
  * into per-row and per-key mask bounds on the device, once per step, so the
@@ -140,7 +141,20 @@ bd_status blockdiag_validate(const int32_t *cu_seqlens_q, const int32_t *cu_seql
  *               (row_lo = row_hi = 0 on padding rows);
  *             key_qlo[batch][seq_len], key_qhi[batch][seq_len]: key position
  *               j of row b is attended by local rows key_qlo <= t < key_qhi
- *               (both 0 when no local row attends it).
+ *               (both 0 when no local row attends it);
+ *             q_order[batch * ceil(q_len / 32)]: a launch order of the
+ *               32-row query tiles, a permutation of the codes b * n_qt + qt
+ *               sorted by the number of 32-key tiles each visits, most first
+ *               (ties in ascending code order); then q_stats[2]: the largest
+ *               and the total visit count (saturated at 2^31 - 1).  Present
+ *               for at most 8192 query tiles over the batch; the order is
+ *               written for tables of at most 2047 segments (larger ones get
+ *               statistics {0, 2^31 - 1}, which no kernel follows).  The
+ *               forward and dQ kernels launch their tiles in this order when
+ *               the largest visit count is at least half of one workgroup
+ *               slot's share of the total (then the launch order sets the
+ *               tail), otherwise last tiles first; results do not depend on
+ *               the order.
  * The table is not re-validated here (that needs a sync); the kernel clamps
  * every bound to its row so a corrupt table cannot make later kernels read
  * out of bounds.  Errors: BD_ERR_INVALID_ARG, BD_ERR_HIP.

@@ -158,6 +158,18 @@ class SegTable:
                                         self.row_offset, self.q_len, meta.data_ptr(), stream))
         return dataclasses.replace(self, table=table, meta=meta, _pinned=pinned)
 
+    def q_order(self):
+        """(order, stats) views of the device metadata: the launch order of
+        the 32-row query tiles (codes b * n_qt + qt, most key tiles visited
+        first) and [largest, total] visits; None when the batch has more
+        than 8192 query tiles (no order is built)."""
+        B, S, L = self.batch, self.seq_len, self.q_len
+        nq = B * ((L + 31) // 32)
+        if not 0 < nq <= 8192:
+            return None
+        o = 2 * B * L + 2 * B * S
+        return self.meta[o:o + nq], self.meta[o + nq:o + nq + 2]
+
     def meta_views(self):
         """(row_lo, row_hi, key_qlo, key_qhi) views of the device metadata."""
         B, S, L = self.batch, self.seq_len, self.q_len

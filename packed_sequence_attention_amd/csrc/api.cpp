@@ -76,7 +76,9 @@ extern "C" bd_status blockdiag_mark_main_kernel(void* start_event, void* stop_ev
 
 extern "C" size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_len) {
   if (batch < 0 || seq_len < 0 || q_len < 0) return 0;
-  return 2 * static_cast<size_t>(batch) * q_len + 2 * static_cast<size_t>(batch) * seq_len;
+  // row bounds, key bounds, then the query- and key-tile orders
+  return 2 * static_cast<size_t>(batch) * q_len + 2 * static_cast<size_t>(batch) * seq_len +
+         bd::meta_order_ints(batch, seq_len, q_len);
 }
 
 extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, int32_t n_seg, int32_t batch,

@@ -37,6 +37,7 @@ namespace bd {
 namespace {
 
 constexpr int kBM = 32;  // query rows per workgroup
+static_assert(kBM == kOrderQB, "the metadata's query-tile order is built for this tile size");
 // Keys per tile: 64, or 32 at head_dim 256 (two 32 KB stages).
 template <int D>
 constexpr int kBNd = D == 256 ? 32 : 64;
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ o,
     const float* __restrict__ lse, float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dq,
-    int n_qt, int n_hg) {
+    int n_qt, int n_hg, int slots) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int kBN = kBNd<D>;
@@ -93,11 +94,29 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
 
-  // Longest-first: the last query tiles of a row have the longest key ranges.
-  const int per_qt = s.batch * n_hg;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
-  const int rem = static_cast<int>(blockIdx.x) % per_qt;
-  const int b = rem / n_hg, hg = rem % n_hg;
+  // Launch order: the last query tiles of the chunk first (neighbouring
+  // workgroups share K/V tiles); when the metadata's statistics say the
+  // longest tile is long against a slot's share of the work (order_pays),
+  // the tiles with the most key tiles to visit first instead (the order the
+  // metadata build sorted).  All n_hg head groups of a tile are adjacent.
+  int qt, b;
+  const int hg = static_cast<int>(blockIdx.x) % n_hg;
+  bool sorted = false;
+  int code = 0;
+  if (m.q_order != nullptr) {
+    code = __builtin_amdgcn_readfirstlane(m.q_order[static_cast<int>(blockIdx.x) / n_hg]);
+    sorted = order_pays(__builtin_amdgcn_readfirstlane(m.q_stats[0]), __builtin_amdgcn_readfirstlane(m.q_stats[1]),
+                        n_hg, slots);
+  }
+  if (sorted) {
+    if (code < 0 || code >= s.batch * n_qt) return;  // whole workgroup: no barrier has been reached
+    b = code / n_qt;
+    qt = code % n_qt;
+  } else {
+    const int per_qt = s.batch * n_hg;
+    qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+    b = (static_cast<int>(blockIdx.x) % per_qt) / n_hg;
+  }
   const int h = hg * 4 + wave;
   const int g = (hg * 4) / s.group;
 
@@ -343,7 +362,8 @@ hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
   bwd_dq_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o),
-      static_cast<const uint16_t*>(a.o), a.lse, a.rowstat, m, static_cast<uint16_t*>(a.dq), n_qt, n_hg);
+      static_cast<const uint16_t*>(a.o), a.lse, a.rowstat, m, static_cast<uint16_t*>(a.dq), n_qt, n_hg,
+      device_cu_count() * kDqOcc<D>);
   return hipGetLastError();
 }
 

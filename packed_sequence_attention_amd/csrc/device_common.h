@@ -91,11 +91,39 @@ struct AttnShape {
   float scale;
 };
 
+// Query-tile order: the metadata build also writes, for the 32-row query
+// tiles of every batch row (the forward and dQ kernels' tiles), a
+// permutation of the tile codes b * n_qt + qt sorted by the number of key
+// tiles of 32 each visits, most first (ties keep ascending code order), and
+// two statistics: the largest visit count and their sum.  A kernel follows
+// the order when its longest tile is long against the load of a workgroup
+// slot (order_pays), since then the launch order sets the tail; otherwise
+// it keeps its fixed order, whose neighbouring tiles share K/V tiles in L2.
+// Built only for at most kOrderCap query tiles over the batch.
+constexpr int kOrderQB = 32;
+constexpr int kOrderCap = 8192;
+
+__host__ __device__ inline int64_t order_q_tiles(int batch, int q_len) {
+  return static_cast<int64_t>(batch) * ((q_len + kOrderQB - 1) / kOrderQB);
+}
+__host__ __device__ inline bool order_built(int batch, int q_len) {
+  const int64_t nq = order_q_tiles(batch, q_len);
+  return nq > 0 && nq <= kOrderCap;
+}
+// The order pays when the longest tile's visits are at least half a slot's
+// share of all visits: tiles * head groups spread over `slots` workgroups
+// resident at once.
+__host__ __device__ inline bool order_pays(int max_visits, int total_visits, int head_groups, int slots) {
+  return 2 * static_cast<int64_t>(max_visits) * slots >= static_cast<int64_t>(total_visits) * head_groups;
+}
+
 struct MetaView {
   const int32_t* row_lo;   // [batch][q_len]
   const int32_t* row_hi;   // [batch][q_len]
   const int32_t* key_qlo;  // [batch][seq_len]
   const int32_t* key_qhi;  // [batch][seq_len]
+  const int32_t* q_order;  // [batch * n_qt] tile codes, most visits first (null: not built)
+  const int32_t* q_stats;  // [2] largest and total visits (null: not built)
 };
 
 __host__ __device__ inline MetaView meta_view(const int32_t* meta, int batch, int seq_len, int q_len) {
@@ -106,6 +134,9 @@ __host__ __device__ inline MetaView meta_view(const int32_t* meta, int batch, in
   m.row_hi = meta + nr;
   m.key_qlo = meta + 2 * nr;
   m.key_qhi = meta + 2 * nr + nk;
+  const bool ord = order_built(batch, q_len);
+  m.q_order = ord ? meta + 2 * nr + 2 * nk : nullptr;
+  m.q_stats = ord ? m.q_order + order_q_tiles(batch, q_len) : nullptr;
   return m;
 }
 

@@ -48,6 +48,7 @@ namespace {
 
 constexpr int kBN = 32;  // keys per tile
 constexpr int kBM = 32;  // query rows per workgroup (one per lane pair)
+static_assert(kBM == kOrderQB, "the metadata's query-tile order is built for this tile size");
 
 template <int D>
 struct FwdLds {
@@ -87,7 +88,8 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, MetaView m,
                                                           uint16_t* __restrict__ o,
-                                                          float* __restrict__ lse, int n_qt, int n_hg) {
+                                                          float* __restrict__ lse, int n_qt, int n_hg,
+                                                          int slots) {
   constexpr int KK = D / 16;  // k-steps of Q K^T
   constexpr int DB = D / 32;  // 32-wide blocks of O^T
   constexpr int CH = D / 8;   // 16-byte chunks per K/V row
@@ -103,11 +105,29 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
 
-  // Longest-first: the last query tiles of a row have the longest key ranges.
-  const int per_qt = s.batch * n_hg;
-  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
-  const int rem = static_cast<int>(blockIdx.x) % per_qt;
-  const int b = rem / n_hg, hg = rem % n_hg;
+  // Launch order: the last query tiles of the chunk first (neighbouring
+  // workgroups share K/V tiles); when the metadata's statistics say the
+  // longest tile is long against a slot's share of the work (order_pays),
+  // the tiles with the most key tiles to visit first instead (the order the
+  // metadata build sorted).  All n_hg head groups of a tile are adjacent.
+  int qt, b;
+  const int hg = static_cast<int>(blockIdx.x) % n_hg;
+  bool sorted = false;
+  int code = 0;
+  if (m.q_order != nullptr) {
+    code = __builtin_amdgcn_readfirstlane(m.q_order[static_cast<int>(blockIdx.x) / n_hg]);
+    sorted = order_pays(__builtin_amdgcn_readfirstlane(m.q_stats[0]), __builtin_amdgcn_readfirstlane(m.q_stats[1]),
+                        n_hg, slots);
+  }
+  if (sorted) {
+    if (code < 0 || code >= s.batch * n_qt) return;  // whole workgroup: no barrier has been reached
+    b = code / n_qt;
+    qt = code % n_qt;
+  } else {
+    const int per_qt = s.batch * n_hg;
+    qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+    b = (static_cast<int>(blockIdx.x) % per_qt) / n_hg;
+  }
   const int h = hg * 4 + wave;
   const int g = (hg * 4) / s.group;
 
@@ -349,7 +369,8 @@ hipError_t fwd_mfma_t(const FwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   fwd_mfma_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-      static_cast<const uint16_t*>(a.v), m, static_cast<uint16_t*>(a.o), a.lse, n_qt, n_hg);
+      static_cast<const uint16_t*>(a.v), m, static_cast<uint16_t*>(a.o), a.lse, n_qt, n_hg,
+      device_cu_count() * kFwdOcc<D>);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return mark(a.mark_stop, st);

@@ -49,6 +49,11 @@ constexpr int kInlineSeg = 126;
 constexpr int kInlineTableInts = 3 * kInlineSeg + 2;
 hipError_t launch_meta_build(const int32_t* table, bool host_table, int n_seg, int batch, int seq_len,
                              int row_offset, int q_len, int32_t* d_meta, hipStream_t stream);
+// int32 entries of the query-tile order and its statistics that follow the
+// bounds in the metadata buffer.
+size_t meta_order_ints(int batch, int seq_len, int q_len);
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 // Generic kernels: any head_dim <= 256 that is a multiple of 8, f32 or bf16.
 hipError_t launch_fwd_generic(const FwdArgs& a, hipStream_t stream);

@@ -24,9 +24,10 @@ __device__ __forceinline__ int upper_index(const int32_t* a, int n, int64_t x) {
   return lo;
 }
 
-// Row idx (of batch * q_len): the key interval [lo, hi) it attends.
-__device__ __forceinline__ void row_bounds(const int32_t* table, int n_seg, int seq_len, int row_offset,
-                                           int q_len, int64_t idx, int32_t* lo_out, int32_t* hi_out) {
+// Row idx (of batch * q_len) in segment s (the largest s with
+// cu_q[s] <= idx): the key interval [lo, hi) it attends.
+__device__ __forceinline__ void row_bounds_in(const int32_t* table, int n_seg, int seq_len, int row_offset,
+                                              int q_len, int64_t idx, int s, int32_t* lo_out, int32_t* hi_out) {
   const int32_t* cu_q = table;
   const int32_t* cu_k = table + n_seg + 1;
   const int32_t* kb = table + 2 * (n_seg + 1);
@@ -35,7 +36,6 @@ __device__ __forceinline__ void row_bounds(const int32_t* table, int n_seg, int 
   const int pos = row_offset + t;
   int lo = 0, hi = 0;
   if (n_seg > 0) {
-    const int s = upper_index(cu_q, n_seg, idx);
     const int qn = cu_q[s + 1] - cu_q[s];
     const int kn = cu_k[s + 1] - cu_k[s];
     if (kn > 0) {
@@ -50,6 +50,20 @@ __device__ __forceinline__ void row_bounds(const int32_t* table, int n_seg, int 
   }
   *lo_out = lo;
   *hi_out = hi;
+}
+
+// Row idx (of batch * q_len): the key interval [lo, hi) it attends.
+__device__ __forceinline__ void row_bounds(const int32_t* table, int n_seg, int seq_len, int row_offset,
+                                           int q_len, int64_t idx, int32_t* lo_out, int32_t* hi_out) {
+  const int s = n_seg > 0 ? upper_index(table, n_seg, idx) : 0;
+  row_bounds_in(table, n_seg, seq_len, row_offset, q_len, idx, s, lo_out, hi_out);
+}
+
+// From a segment s with cu_q[s] <= idx, the largest such s (a forward walk:
+// one thread visits increasing rows).
+__device__ __forceinline__ int walk_index(const int32_t* cu_q, int n_seg, int64_t idx, int s) {
+  while (s + 1 < n_seg && cu_q[s + 1] <= idx) ++s;
+  return s;
 }
 
 // Key idx (of batch * seq_len): the interval [qlo, qhi) of local rows
@@ -84,11 +98,133 @@ __device__ __forceinline__ void key_bounds(const int32_t* table, int n_seg, int 
   *qhi_out = qhi;
 }
 
+// Work bin of a tile that visits w tiles of the other kind: exact below 128,
+// then 16 bins per octave (bins rise with w; 255 from 2^15 up).
+__device__ __forceinline__ int work_bin(int w) {
+  if (w < 128) return w < 0 ? 0 : w;
+  const int e = 31 - __builtin_clz(static_cast<unsigned>(w));
+  const int bin = 128 + (e - 7) * 16 + ((w >> (e - 4)) & 15);
+  return bin > 255 ? 255 : bin;
+}
+
+// Number of bytes of x equal to zero (exact: no borrow between bytes).
+__device__ __forceinline__ int zero_bytes(uint32_t x, uint32_t keep) {
+  const uint32_t z = ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x | 0x7F7F7F7Fu);
+  return __builtin_popcount(z & keep);
+}
+
+// The query-tile order and its statistics, built by one workgroup of 256
+// threads from the segment table.  Query tile (b, qt) covers local rows
+// [32 qt, 32 qt + 32); its rows attend keys from doc_start of its first row
+// to the position of its last real row (padding rows are the tail of a
+// chunk), so it visits last/32 - lo/32 + 1 key tiles of 32 (none when its
+// first row is padding).  A stable counting sort on the visit bins
+// (descending) places the codes b * n_qt + qt: ties keep ascending order.
+struct OrderLds {
+  uint8_t bin[kOrderCap];
+  int hist[256];
+  int scan[256];
+  int vmax;
+  unsigned long long vsum;
+};
+
+__device__ void build_q_order(const int32_t* table, int n_seg, int batch, int seq_len, int row_offset,
+                              int q_len, MetaView m, OrderLds& ol) {
+  const int tid = threadIdx.x;
+  uint8_t* bins = ol.bin;
+  int* hist = ol.hist;
+  int* scan = ol.scan;
+  const int32_t* cu_q = table;
+  const int32_t* cu_k = table + n_seg + 1;
+  const int n_qt = (q_len + kOrderQB - 1) / kOrderQB;
+  const int nq = batch * n_qt;
+  hist[tid] = 0;
+  if (tid == 0) {
+    ol.vmax = 0;
+    ol.vsum = 0;
+  }
+  __syncthreads();
+  int vmax = 0;
+  unsigned long long vsum = 0;
+  // Each thread takes a contiguous run of tile codes: their rows increase,
+  // so one binary search and then a forward walk find every segment.
+  const int per = (nq + 255) / 256;
+  const int i0 = min(nq, tid * per), i1 = min(nq, i0 + per);
+  int seg = (n_seg > 0 && i0 < i1)
+                ? upper_index(cu_q, n_seg, static_cast<int64_t>(i0 / n_qt) * q_len + (i0 % n_qt) * kOrderQB)
+                : 0;
+  for (int i = i0; i < i1; ++i) {
+    const int b = i / n_qt, qt = i % n_qt;
+    int tiles = 0;
+    if (n_seg > 0) {
+      const int t0 = qt * kOrderQB, t1 = min(q_len, t0 + kOrderQB);
+      const int64_t r0 = static_cast<int64_t>(b) * q_len + t0;
+      seg = walk_index(cu_q, n_seg, r0, seg);
+      int lo, hi;
+      row_bounds_in(table, n_seg, seq_len, row_offset, q_len, r0, seg, &lo, &hi);
+      if (hi > lo) {
+        const int s1 = walk_index(cu_q, n_seg, static_cast<int64_t>(b) * q_len + t1 - 1, seg);
+        const int last = cu_k[s1 + 1] - cu_k[s1] > 0
+                             ? row_offset + t1 - 1
+                             : row_offset + static_cast<int>(cu_q[s1] - static_cast<int64_t>(b) * q_len) - 1;
+        tiles = max(0, last / kOrderQB - lo / kOrderQB + 1);
+      }
+    }
+    const int bin = work_bin(tiles);
+    bins[i] = static_cast<uint8_t>(bin);
+    atomicAdd(&hist[bin], 1);
+    vmax = max(vmax, tiles);
+    vsum += static_cast<unsigned long long>(tiles);
+  }
+  atomicMax(&ol.vmax, vmax);
+  atomicAdd(&ol.vsum, vsum);
+  __syncthreads();
+  if (tid == 0) {
+    int32_t* st = const_cast<int32_t*>(m.q_stats);
+    st[0] = ol.vmax;
+    st[1] = static_cast<int32_t>(ol.vsum < 0x7FFFFFFFull ? ol.vsum : 0x7FFFFFFFull);  // saturated
+  }
+  // Exclusive scan over the bins in descending order: thread t holds bin
+  // 255 - t; its tiles start after those of every higher bin.
+  const int v = hist[255 - tid];
+  scan[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int x = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += x;
+    __syncthreads();
+  }
+  hist[255 - tid] = scan[tid] - v;  // first position of each bin
+  __syncthreads();
+  // Stable placement, 256 codes at a time: a code's position is its bin's
+  // next free position plus the number of earlier codes of this chunk in
+  // the same bin (bins compared four bytes at a time).
+  int32_t* out = const_cast<int32_t*>(m.q_order);
+  for (int c0 = 0; c0 < nq; c0 += 256) {
+    const int i = c0 + tid;
+    const bool has = i < nq;
+    const int bin = has ? bins[i] : 0;
+    int rank = 0;
+    if (has) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(bins + c0);
+      const uint32_t rep = static_cast<uint32_t>(bin) * 0x01010101u;
+      for (int k = 0; k < (tid >> 2); ++k) rank += zero_bytes(w[k] ^ rep, 0xFFFFFFFFu);
+      if (tid & 3) rank += zero_bytes(w[tid >> 2] ^ rep, (1u << (8 * (tid & 3))) - 1u);
+      out[hist[bin] + rank] = i;
+    }
+    __syncthreads();  // every position of this chunk read before the bins advance
+    if (has) atomicAdd(&hist[bin], 1);
+    __syncthreads();
+  }
+}
+
 // One launch for both halves: threads [0, n_rows) write row bounds, the
-// rest key bounds.
+// rest key bounds.  `block` is the workgroup's index among those doing this.
 __device__ __forceinline__ void meta_one(const int32_t* table, int n_seg, int seq_len, int row_offset,
-                                         int q_len, int64_t n_rows, int64_t n_keys, MetaView m) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+                                         int q_len, int64_t n_rows, int64_t n_keys, MetaView m,
+                                         int64_t block) {
+  const int64_t idx = block * blockDim.x + threadIdx.x;
   if (idx < n_rows) {
     row_bounds(table, n_seg, seq_len, row_offset, q_len, idx, const_cast<int32_t*>(m.row_lo) + idx,
                const_cast<int32_t*>(m.row_hi) + idx);
@@ -99,9 +235,36 @@ __device__ __forceinline__ void meta_one(const int32_t* table, int n_seg, int se
   }
 }
 
-__global__ void meta_kernel(const int32_t* __restrict__ table, int n_seg, int seq_len, int row_offset,
+// With the query-tile order built (m.q_order non-null), workgroup 0 builds
+// it and the others (one more than the bounds need) write the bounds.
+
+// Tables of up to this many segments are staged in LDS by the workgroup
+// that builds the query-tile order (its binary searches would otherwise wait
+// on global memory at every step); larger ones get no sorted order.
+constexpr int kOrderStageSeg = 2047;
+
+__global__ void meta_kernel(const int32_t* __restrict__ table, int n_seg, int batch, int seq_len, int row_offset,
                             int q_len, int64_t n_rows, int64_t n_keys, MetaView m) {
-  meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
+  __shared__ OrderLds ol;
+  __shared__ int32_t stage[3 * kOrderStageSeg + 2];
+  if (m.q_order != nullptr) {
+    if (blockIdx.x == 0) {
+      if (n_seg <= kOrderStageSeg) {
+        for (int i = threadIdx.x; i < 3 * n_seg + 2; i += blockDim.x) stage[i] = table[i];
+        __syncthreads();
+        build_q_order(stage, n_seg, batch, seq_len, row_offset, q_len, m, ol);
+      } else if (threadIdx.x == 0) {
+        // statistics that no kernel takes as a reason to follow the order
+        int32_t* st = const_cast<int32_t*>(m.q_stats);
+        st[0] = 0;
+        st[1] = 0x7FFFFFFF;
+      }
+      return;
+    }
+    meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, static_cast<int64_t>(blockIdx.x) - 1);
+  } else {
+    meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, blockIdx.x);
+  }
 }
 
 // The table passed by value in the kernel arguments (small tables): no
@@ -110,13 +273,22 @@ struct InlineTable {
   int32_t v[kInlineTableInts];
 };
 
-__global__ void meta_inline_kernel(InlineTable tab, int n_seg, int seq_len, int row_offset, int q_len,
+__global__ void meta_inline_kernel(InlineTable tab, int n_seg, int batch, int seq_len, int row_offset, int q_len,
                                    int64_t n_rows, int64_t n_keys, MetaView m) {
   __shared__ int32_t sh[kInlineTableInts];
+  __shared__ OrderLds ol;
   const int n_int = 3 * n_seg + 2;
   for (int i = threadIdx.x; i < n_int; i += blockDim.x) sh[i] = tab.v[i];
   __syncthreads();
-  meta_one(sh, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
+  if (m.q_order != nullptr) {
+    if (blockIdx.x == 0) {
+      build_q_order(sh, n_seg, batch, seq_len, row_offset, q_len, m, ol);
+      return;
+    }
+    meta_one(sh, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, static_cast<int64_t>(blockIdx.x) - 1);
+  } else {
+    meta_one(sh, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, blockIdx.x);
+  }
 }
 
 }  // namespace
@@ -128,16 +300,36 @@ hipError_t launch_meta_build(const int32_t* table, bool host_table, int n_seg, i
   const int64_t n_keys = static_cast<int64_t>(batch) * seq_len;
   const int64_t n = n_rows + n_keys;
   if (n == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  // one more workgroup (the first) builds the query-tile order
+  dim3 grid(static_cast<unsigned>((n + 255) / 256 + (m.q_order != nullptr ? 1 : 0)));
   if (host_table) {
     InlineTable tab;
     const int n_int = 3 * n_seg + 2;
     for (int i = 0; i < kInlineTableInts; ++i) tab.v[i] = i < n_int ? table[i] : 0;
-    meta_inline_kernel<<<grid, 256, 0, stream>>>(tab, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
+    meta_inline_kernel<<<grid, 256, 0, stream>>>(tab, n_seg, batch, seq_len, row_offset, q_len, n_rows, n_keys,
+                                                 m);
   } else {
-    meta_kernel<<<grid, 256, 0, stream>>>(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m);
+    meta_kernel<<<grid, 256, 0, stream>>>(table, n_seg, batch, seq_len, row_offset, q_len, n_rows, n_keys, m);
   }
   return hipGetLastError();
+}
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+size_t meta_order_ints(int batch, int seq_len, int q_len) {
+  (void)seq_len;
+  // the order, then its two statistics, when an order is built
+  return order_built(batch, q_len) ? static_cast<size_t>(order_q_tiles(batch, q_len)) + 2 : 0;
 }
 
 }  // namespace bd

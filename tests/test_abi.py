@@ -166,7 +166,8 @@ def test_attention_entry_points_reject_before_launch():
     assert b"workspace" in lib.blockdiag_last_error()
     # metadata build rejects an empty table for a non-empty chunk
     assert lib.blockdiag_meta_build(p, 0, 1, 64, 0, 64, p, N) == 2
-    assert lib.blockdiag_meta_ints(2, 100, 40) == 2 * 2 * 40 + 2 * 2 * 100
+    # bounds of rows and keys, then the order of the 32-row query tiles and its two statistics
+    assert lib.blockdiag_meta_ints(2, 100, 40) == 2 * 2 * 40 + 2 * 2 * 100 + 2 * 2 + 2
 
 
 def test_meta_build_host_rejects_before_launch():

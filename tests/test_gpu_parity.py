@@ -66,6 +66,58 @@ def test_metadata_bit_exact_random_layouts():
             np.testing.assert_array_equal(g_, r_)
 
 
+def _work_bin(w):
+    """Work bins of the launch orders: exact below 128, then 16 per octave."""
+    w = np.maximum(np.asarray(w, np.int64), 0)
+    e = np.floor(np.log2(np.maximum(w, 1))).astype(np.int64)
+    hi = 128 + (e - 7) * 16 + ((w >> np.maximum(e - 4, 0)) & 15)
+    return np.where(w < 128, w, np.minimum(hi, 255))
+
+
+def _expected_visits(bounds, row_offset):
+    """Key tiles of 32 each 32-row query tile visits (from doc_start of its
+    first real row to its last real row; 0 for an all-padding tile), from the
+    oracle's mask bounds, in tile-code order b * n_qt + qt."""
+    row_lo, row_hi = bounds[0], bounds[1]
+    out = []
+    for b in range(row_lo.shape[0]):
+        for t0 in range(0, row_lo.shape[1], 32):
+            real = np.nonzero(row_hi[b, t0:t0 + 32] > row_lo[b, t0:t0 + 32])[0]
+            out.append(0 if len(real) == 0 else
+                       (row_offset + t0 + real.max()) // 32 - row_lo[b, t0 + real.min()] // 32 + 1)
+    return np.array(out, np.int64)
+
+
+@gpu
+@pytest.mark.parametrize("case", range(7))
+def test_query_tile_order(case):
+    """The metadata's query-tile launch order: a permutation of the tile
+    codes, visit bins non-increasing along it with ties in ascending code
+    order, and statistics [largest, total] equal to those of the visit counts
+    computed from the oracle's mask bounds (five workloads and two chunked,
+    padded layouts)."""
+    import packed_sequence_attention_amd as bd
+    from oracle import segment as SEG
+    if case < 5:
+        w = synthetic.workload(synthetic.WORKLOADS[case])
+        rows, S, r0, L = w.doc_lens, w.seq_len, w.row_offset, w.q_len
+    elif case == 5:
+        rows, S, r0, L = [[300, 40, 500, 100], [1000], [7, 9, 600]], 1024, 256, 512
+    else:
+        rows, S, r0, L = [[5000, 3000, 100], [64] * 100], 9000, 4000, 4200
+    _log(f"query-tile order case {case}")
+    seg = bd.segment(rows, S, r0, L, device="cuda")
+    order, stats = seg.q_order()
+    visits = _expected_visits(SEG.mask_bounds_np(rows, S, r0, L), r0)
+    g = order.cpu().numpy().astype(np.int64)
+    np.testing.assert_array_equal(np.sort(g), np.arange(len(visits)))
+    bins = _work_bin(visits)[g]
+    assert np.all(np.diff(bins) <= 0)
+    same = np.diff(bins) == 0
+    assert np.all(np.diff(g)[same] > 0)
+    np.testing.assert_array_equal(stats.cpu().numpy(), [visits.max(), visits.sum()])
+
+
 @gpu
 def test_metadata_inline_and_device_tables_agree():
     """The table passed by value in the launch arguments and the table copied
