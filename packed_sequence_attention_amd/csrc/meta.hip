@@ -121,7 +121,7 @@ __device__ __forceinline__ int zero_bytes(uint32_t x, uint32_t keep) {
 // first row is padding).  A stable counting sort on the visit bins
 // (descending) places the codes b * n_qt + qt: ties keep ascending order.
 struct OrderLds {
-  uint8_t bin[kOrderCap];
+  alignas(16) uint8_t bin[kOrderCap];
   int hist[256];
   int scan[256];
   int vmax;
@@ -185,17 +185,21 @@ __device__ void build_q_order(const int32_t* table, int n_seg, int batch, int se
     st[1] = static_cast<int32_t>(ol.vsum < 0x7FFFFFFFull ? ol.vsum : 0x7FFFFFFFull);  // saturated
   }
   // Exclusive scan over the bins in descending order: thread t holds bin
-  // 255 - t; its tiles start after those of every higher bin.
+  // 255 - t; its tiles start after those of every higher bin.  Inclusive
+  // scan inside each wave (shuffles), then the totals of the waves before.
   const int v = hist[255 - tid];
-  scan[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int x = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += x;
-    __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int x = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += x;
   }
-  hist[255 - tid] = scan[tid] - v;  // first position of each bin
+  if (lane == 63) scan[wv] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int k = 0; k < wv; ++k) before += scan[k];
+  hist[255 - tid] = before + inc - v;  // first position of each bin
   __syncthreads();
   // Stable placement, 256 codes at a time: a code's position is its bin's
   // next free position plus the number of earlier codes of this chunk in
@@ -207,10 +211,23 @@ __device__ void build_q_order(const int32_t* table, int n_seg, int batch, int se
     const int bin = has ? bins[i] : 0;
     int rank = 0;
     if (has) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(bins + c0);
+      // all 256 bytes of the chunk in 16 reads of 16 bytes, issued together;
+      // only bytes before this code's count
+      const uint4* w = reinterpret_cast<const uint4*>(bins + c0);
       const uint32_t rep = static_cast<uint32_t>(bin) * 0x01010101u;
-      for (int k = 0; k < (tid >> 2); ++k) rank += zero_bytes(w[k] ^ rep, 0xFFFFFFFFu);
-      if (tid & 3) rank += zero_bytes(w[tid >> 2] ^ rep, (1u << (8 * (tid & 3))) - 1u);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint4 q = w[k];
+        const uint32_t words[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int wi = 4 * k + e;  // bytes 4 wi .. 4 wi + 3 of the chunk
+          const uint32_t keep = wi < (tid >> 2)    ? 0xFFFFFFFFu
+                                : wi == (tid >> 2) ? (1u << (8 * (tid & 3))) - 1u
+                                                   : 0u;
+          rank += zero_bytes(words[e] ^ rep, keep);
+        }
+      }
       out[hist[bin] + rank] = i;
     }
     __syncthreads();  // every position of this chunk read before the bins advance
