@@ -11,6 +11,9 @@
   activation checkpointing equals the original, Design overview, packed.py);
 * documents are independent: changing one document's inputs leaves every
   other document's O, LSE, dK and dV bit for bit unchanged;
+* the launch order does not change a result: the forward and dQ kernels
+  run their query tiles longest first when the metadata's statistics say
+  so, otherwise in a fixed order; both give the same bits;
 * the autograd wrapper returns the raw calls' results.
 """
 import numpy as np
@@ -98,6 +101,34 @@ def test_determinism():
     g1 = bd.attn_bwd(d["q"], d["k"], d["v"], o1, l1, d["do"], seg)
     g2 = bd.attn_bwd(d["q"], d["k"], d["v"], o1, l1, d["do"], seg)
     assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+
+
+@gpu
+@pytest.mark.parametrize("wid", [2, 3])
+def test_launch_order_does_not_change_results(wid):
+    """Workloads 2 and 3 meet the condition for the longest-first order of the
+    query tiles; overwriting the metadata's visit statistics with values no
+    kernel follows ({0, 2^31 - 1}) makes the same calls run in the fixed
+    order, and every output is identical bit for bit."""
+    import torch
+    import packed_sequence_attention_amd as bd
+    w = synthetic.workload(wid)
+    t = synthetic.draw_tensors(w)
+    d = H.to_device(w, t)
+    seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device="cuda")
+    _, stats = seg.q_order()
+    st = stats.cpu().numpy()
+    n_hg, slots = w.h_q // 4, 256 * 2  # the dQ kernel's slots on 256 CUs (the forward has more)
+    assert 2 * int(st[0]) * slots >= int(st[1]) * n_hg, "the sorted order is expected to be followed here"
+    o1, l1 = bd.attn_fwd(d["q"], d["k"], d["v"], seg)
+    g1 = bd.attn_bwd(d["q"], d["k"], d["v"], o1, l1, d["do"], seg)
+    stats.copy_(torch.tensor([0, 2**31 - 1], dtype=torch.int32, device=stats.device))
+    o2, l2 = bd.attn_fwd(d["q"], d["k"], d["v"], seg)
+    g2 = bd.attn_bwd(d["q"], d["k"], d["v"], o2, l2, d["do"], seg)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
 
 
 @gpu
