@@ -145,17 +145,18 @@ class SegTable:
         flat = np.ascontiguousarray(np.concatenate([self.cu_q, self.cu_k, self.k_begin]), dtype=np.int32)
         n_meta = lib.blockdiag_meta_ints(self.batch, self.seq_len, self.q_len)
         meta = torch.empty(max(int(n_meta), 1), dtype=torch.int32, device=device)
-        stream = torch.cuda.current_stream(device).cuda_stream
+        stream = torch.cuda.current_stream(meta.device).cuda_stream
         if inline is None:
             inline = self.n_seg <= lib.blockdiag_meta_inline_max_seg()
-        if inline:
-            _check(lib.blockdiag_meta_build_host(_ptr(flat), self.n_seg, self.batch, self.seq_len,
-                                                 self.row_offset, self.q_len, meta.data_ptr(), stream))
-            return dataclasses.replace(self, table=None, meta=meta, _pinned=None)
-        pinned = torch.from_numpy(flat).pin_memory()
-        table = pinned.to(device, non_blocking=True)  # no host sync; pinned copy kept alive below
-        _check(lib.blockdiag_meta_build(table.data_ptr(), self.n_seg, self.batch, self.seq_len,
-                                        self.row_offset, self.q_len, meta.data_ptr(), stream))
+        with torch.cuda.device(meta.device):  # the library launches on the current device
+            if inline:
+                _check(lib.blockdiag_meta_build_host(_ptr(flat), self.n_seg, self.batch, self.seq_len,
+                                                     self.row_offset, self.q_len, meta.data_ptr(), stream))
+                return dataclasses.replace(self, table=None, meta=meta, _pinned=None)
+            pinned = torch.from_numpy(flat).pin_memory()
+            table = pinned.to(meta.device, non_blocking=True)  # no host sync; pinned copy kept alive below
+            _check(lib.blockdiag_meta_build(table.data_ptr(), self.n_seg, self.batch, self.seq_len,
+                                            self.row_offset, self.q_len, meta.data_ptr(), stream))
         return dataclasses.replace(self, table=table, meta=meta, _pinned=pinned)
 
     def q_order(self):
@@ -270,9 +271,11 @@ def _shapes(q, k, v, seg):
     if Bk != B or dk != d or B != seg.batch or S != seg.seq_len or L != seg.q_len:
         raise BlockdiagError(1, f"shapes q{tuple(q.shape)} k{tuple(k.shape)} do not match the "
                                 f"segment table (B={seg.batch}, S={seg.seq_len}, q_len={seg.q_len})")
+    if q.device.type != "cuda":
+        raise BlockdiagError(1, "q, k, v must be contiguous device tensors of one dtype")
     for t in (q, k, v):
-        if not t.is_contiguous() or t.device.type != "cuda" or t.dtype != q.dtype:
-            raise BlockdiagError(1, "q, k, v must be contiguous device tensors of one dtype")
+        if not t.is_contiguous() or t.device != q.device or t.dtype != q.dtype:
+            raise BlockdiagError(1, "q, k, v must be contiguous device tensors of one dtype on one device")
     if seg.meta is None or seg.meta.device != q.device:
         raise BlockdiagError(1, "segment table has no device metadata on the tensors' device")
     return B, L, Hq, d, S, Hkv
@@ -297,9 +300,10 @@ def attn_fwd(q, k, v, seg, scale=None):
     ws_bytes = lib.blockdiag_workspace_bytes(0, dt, B, S, L, Hq, Hkv, d)
     ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(lib.blockdiag_attn_fwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(), k.data_ptr(),
-                                  v.data_ptr(), seg.meta.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                  ws.data_ptr(), ws_bytes, stream))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        _check(lib.blockdiag_attn_fwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(),
+                                      k.data_ptr(), v.data_ptr(), seg.meta.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), ws.data_ptr(), ws_bytes, stream))
     return o, lse
 
 
@@ -309,10 +313,11 @@ def attn_bwd(q, k, v, o, lse, do, seg, scale=None):
     lib = load_library()
     B, L, Hq, d, S, Hkv = _shapes(q, k, v, seg)
     for t in (o, do):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise BlockdiagError(1, "o and do must match q")
-    if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise BlockdiagError(1, "lse must be contiguous float32 [B, H_q, q_len]")
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise BlockdiagError(1, "o and do must match q (shape, dtype, device, contiguous)")
+    if (lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise BlockdiagError(1, "lse must be contiguous float32 [B, H_q, q_len] on q's device")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _dtype_code(q)
     dq = torch.empty_like(q)
@@ -321,10 +326,11 @@ def attn_bwd(q, k, v, o, lse, do, seg, scale=None):
     ws_bytes = lib.blockdiag_workspace_bytes(1, dt, B, S, L, Hq, Hkv, d)
     ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(lib.blockdiag_attn_bwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(), k.data_ptr(),
-                                  v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                                  seg.meta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                  ws.data_ptr(), ws_bytes, stream))
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        _check(lib.blockdiag_attn_bwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(),
+                                      k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      do.data_ptr(), seg.meta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                      dv.data_ptr(), ws.data_ptr(), ws_bytes, stream))
     return dq, dk, dv
 
 

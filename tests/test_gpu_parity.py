@@ -342,3 +342,45 @@ def test_single_document_spanning_every_chunk(dtype, d):
     errs = H.check(w_full, {"dk": dk_sum, "dv": dv_sum, "dq": full["dq"]},
                    {"dk": full["dk"], "dv": full["dv"], "dq": full["dq"]})
     _log("  summed dK/dV errors", {k: f"{v:.3g}" for k, v in errs.items() if k != "dq"})
+
+
+@gpu
+def test_binding_rejects_mismatched_tensors_before_launch():
+    """The Python binding checks every tensor's shape, dtype, layout and
+    device against q before any kernel is enqueued; nothing is written."""
+    import torch
+
+    import packed_sequence_attention_amd as bd
+    _log("binding argument checks")
+    seg = bd.segment([[40, 24], [64]], 64, 0, 64, device="cuda")
+    q = torch.randn(2, 64, 4, 64, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(2, 64, 2, 64, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn_like(k)
+    o, lse = bd.attn_fwd(q, k, v, seg)
+    do = torch.randn_like(q)
+    bad_fwd = [
+        (q.cpu(), k, v),                      # q off the device
+        (q, k.cpu(), v),                      # k off q's device
+        (q, k, v.float()),                    # dtype mismatch
+        (q, k.transpose(1, 2), v),            # non-contiguous / wrong shape
+        (q[:, :32], k, v),                    # q_len differs from the table
+    ]
+    for args in bad_fwd:
+        with pytest.raises(bd.BlockdiagError):
+            bd.attn_fwd(*args, seg)
+    bad_bwd = [
+        (o.cpu(), lse, do),                   # o off q's device
+        (o, lse.cpu(), do),                   # lse off q's device
+        (o, lse, do.cpu()),                   # dO off q's device
+        (o, lse.double(), do),                # lse dtype
+        (o, lse, do.float()),                 # dO dtype
+        (o, lse[:, :, :32], do),              # lse shape
+    ]
+    for o_, l_, d_ in bad_bwd:
+        with pytest.raises(bd.BlockdiagError):
+            bd.attn_bwd(q, k, v, o_, l_, d_, seg)
+    torch.cuda.synchronize()
+    # the good call still works after the rejected ones
+    dq, dk, dv = bd.attn_bwd(q, k, v, o, lse, do, seg)
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(t.float()).all().item() for t in (dq, dk, dv))
