@@ -132,9 +132,10 @@ def traffic_from_profile(kernel, kernel_file, workload_tag):
 
 def cpu_baseline(w, t, flops_per_pair, budget_s=10.0):
     """The fp64 oracle (windowed, unchanged) timed on this host: batch rows
-    are run one after another (each row's K/V heads as sub-problems over the
-    whole row, forward and backward, in a pool of worker processes with one
-    BLAS thread each) until the rows done so far have taken `budget_s`
+    are run one after another (each row split into (K/V head, query-row
+    range) sub-problems, forward and backward, in a pool of one worker
+    process per allowed core -- capped by OMP_NUM_THREADS when set -- with
+    one BLAS thread each) until the rows done so far have taken `budget_s`
     seconds or the whole workload is done."""
     import numpy as np
     from oracle import parallel
@@ -155,9 +156,10 @@ def cpu_baseline(w, t, flops_per_pair, budget_s=10.0):
         if dt >= budget_s:
             break
     what = "the whole workload" if rows == w.batch else f"batch rows 0..{rows - 1} of {w.batch}"
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": min(workers, w.h_kv),
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{what} (all {w.h_q} query heads), forward+backward, fp64 numpy windowed oracle"}
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
+            "host_cores": parallel.host_cores(), "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{what} (all {w.h_q} query heads), forward+backward, fp64 numpy windowed oracle, "
+                      f"jobs of (K/V head, row range) on {workers} worker processes"}
 
 
 def main():

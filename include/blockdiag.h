@@ -123,6 +123,29 @@ bd_status blockdiag_validate(const int32_t *cu_seqlens_q, const int32_t *cu_seql
                              int32_t seq_len, int32_t row_offset, int32_t q_len);
 
 /*
+ * bd_meta -- host descriptor of a device metadata buffer.  It records the
+ * sizes the buffer was built for, so the attention calls can check in O(1)
+ * on the host that the metadata matches their own sizes before anything is
+ * launched (key property 4: no offset a kernel consumes goes unchecked; the
+ * kernels index the metadata with the call's batch, seq_len and q_len).
+ * Filled only by blockdiag_meta_build / blockdiag_meta_build_host; a caller
+ * treats it as opaque.  It stays valid while the buffer holds what that
+ * build wrote (a later build into the same buffer needs its own
+ * descriptor).  The descriptor holds the device pointer but owns nothing.
+ */
+#define BD_META_MAGIC 0x54454d42u /* "BMET" */
+typedef struct bd_meta {
+  uint32_t magic;       /* BD_META_MAGIC after a successful build, else 0  */
+  int32_t batch;        /* sizes of the chunk the buffer describes         */
+  int32_t seq_len;
+  int32_t row_offset;
+  int32_t q_len;
+  int32_t n_seg;        /* segments of the table it was built from         */
+  uint64_t n_ints;      /* int32 entries written: blockdiag_meta_ints(...) */
+  const int32_t *data;  /* the device buffer (caller-owned)                */
+} bd_meta;
+
+/*
  * blockdiag_meta_ints -- number of int32 in the device metadata buffer that
  * blockdiag_meta_build fills: 2 * batch * q_len + 2 * batch * seq_len,
  * plus nq + 2 with nq = batch * ceil(q_len / 32) when 1 <= nq <= 8192.
@@ -135,7 +158,8 @@ bd_status blockdiag_validate(const int32_t *cu_seqlens_q, const int32_t *cu_seql
  *   d_table   device int32 [3 * n_seg + 2] = cu_seqlens_q[n_seg+1] ++
  *             cu_seqlens_k[n_seg+1] ++ seg_k_begin[n_seg], as produced by
  *             blockdiag_segment and accepted by blockdiag_validate.
- *   d_meta    device int32 [blockdiag_meta_ints(...)], written as
+ *   d_meta    device int32 [meta_capacity] with meta_capacity >=
+ *             blockdiag_meta_ints(...), written as
  *             row_lo[batch][q_len], row_hi[batch][q_len]: local row t of
  *               batch row b attends key positions row_lo <= j < row_hi
  *               (row_lo = row_hi = 0 on padding rows);
@@ -155,14 +179,18 @@ bd_status blockdiag_validate(const int32_t *cu_seqlens_q, const int32_t *cu_seql
  *               slot's share of the total (then the launch order sets the
  *               tail), otherwise last tiles first; results do not depend on
  *               the order.
+ *   desc      (host, required) receives the buffer's descriptor for the
+ *             attention calls; on any error its magic is set to 0.
  * The table is not re-validated here (that needs a sync); the kernel clamps
  * every bound to its row so a corrupt table cannot make later kernels read
- * out of bounds.  Errors: BD_ERR_INVALID_ARG, BD_ERR_HIP.
+ * out of bounds.  Errors: BD_ERR_INVALID_ARG, BD_ERR_CAPACITY (meta_capacity
+ * too small; nothing is launched), BD_ERR_HIP.
  */
 size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_len);
 bd_status blockdiag_meta_build(const int32_t *d_table, int32_t n_seg, int32_t batch,
                                int32_t seq_len, int32_t row_offset, int32_t q_len,
-                               int32_t *d_meta, void *stream);
+                               int32_t *d_meta, size_t meta_capacity, bd_meta *desc,
+                               void *stream);
 
 /*
  * blockdiag_meta_build_host -- blockdiag_meta_build for a table in host
@@ -171,15 +199,17 @@ bd_status blockdiag_meta_build(const int32_t *d_table, int32_t n_seg, int32_t ba
  * during the call and travels to the kernel in its launch arguments, so the
  * step needs no host-to-device copy of it (Summary: per-step precompute,
  * zero per-layer host syncs).  h_table is not retained after the call
- * returns.  d_meta, the output and the stream ordering are as for
- * blockdiag_meta_build.  Errors: BD_ERR_CAPACITY when n_seg exceeds the
- * limit (nothing is launched; use blockdiag_meta_build), BD_ERR_INVALID_ARG,
- * BD_ERR_BAD_METADATA, BD_ERR_HIP.
+ * returns.  d_meta, meta_capacity, desc, the output and the stream ordering
+ * are as for blockdiag_meta_build.  Errors: BD_ERR_CAPACITY when n_seg
+ * exceeds the limit (use blockdiag_meta_build) or meta_capacity is too
+ * small (nothing is launched), BD_ERR_INVALID_ARG, BD_ERR_BAD_METADATA,
+ * BD_ERR_HIP.
  */
 int32_t blockdiag_meta_inline_max_seg(void);
 bd_status blockdiag_meta_build_host(const int32_t *h_table, int32_t n_seg, int32_t batch,
                                     int32_t seq_len, int32_t row_offset, int32_t q_len,
-                                    int32_t *d_meta, void *stream);
+                                    int32_t *d_meta, size_t meta_capacity, bd_meta *desc,
+                                    void *stream);
 
 /*
  * blockdiag_workspace_bytes -- device scratch the forward (is_bwd = 0) or
@@ -191,9 +221,11 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
 /*
  * blockdiag_attn_fwd -- O and LSE of the chunk (Summary: the varlen kernel;
  * Design overview, runtime.py: drop-in SDPA; packed.py: row_offset = 0).
- *   q, k, v (device, dtype) as in the conventions above; d_meta (device) from
- *   blockdiag_meta_build for the same batch/seq_len/row_offset/q_len; o
- *   (device, dtype) and lse (device, float32) are written in full.
+ *   q, k, v (device, dtype) as in the conventions above; meta (host) the
+ *   descriptor blockdiag_meta_build wrote for the same batch, seq_len,
+ *   row_offset and q_len (a descriptor built for other sizes, or not built,
+ *   is rejected with BD_ERR_INVALID_ARG before any launch); o (device,
+ *   dtype) and lse (device, float32) are written in full.
  *   scale multiplies q.k (1/sqrt(head_dim) is the usual choice).
  *   Supported: any head_dim up to 256 that is a multiple of 8, float32 or
  *   bf16, h_q % h_kv = 0.  bf16 with h_q / h_kv a multiple of 4 runs on the
@@ -212,13 +244,15 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
 bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
                              int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
                              float scale, const void *q, const void *k, const void *v,
-                             const int32_t *d_meta, void *o, float *lse, void *workspace,
+                             const bd_meta *meta, void *o, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream);
 
 /*
  * blockdiag_attn_bwd -- dQ, dK, dV of the loss sum(dO * O) for the chunk
  * (Proof section: forward/backward parity and input gradients).  LSE has no
- * incoming gradient.  o and lse are the forward's outputs; d_o like o.
+ * incoming gradient.  o and lse are the forward's outputs; d_o like o;
+ * meta as for blockdiag_attn_fwd (not read, and may be NULL, when q_len or
+ * batch is 0).
  *   dq (device, like q) is written in full; dk, dv (device, like k) are
  *   written for every key of every row -- the chunk's partial gradients, zero
  *   at keys no local row attends, so summing them over the chunks of a row
@@ -235,7 +269,7 @@ bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
                              int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
                              float scale, const void *q, const void *k, const void *v,
                              const void *o, const float *lse, const void *d_o,
-                             const int32_t *d_meta, void *dq, void *dk, void *dv,
+                             const bd_meta *meta, void *dq, void *dk, void *dv,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -34,7 +34,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "BlockdiagError", "SegTable", "segment", "validate", "doc_lens_from_ids",
+    "BlockdiagError", "MetaDesc", "SegTable", "segment", "validate", "doc_lens_from_ids",
     "attn_fwd", "attn_bwd", "attention", "library_path", "load_library",
 ]
 
@@ -48,6 +48,18 @@ EXPORTS = ("blockdiag_segment", "blockdiag_validate", "blockdiag_meta_ints", "bl
            "blockdiag_meta_build_host", "blockdiag_meta_inline_max_seg",
            "blockdiag_workspace_bytes", "blockdiag_attn_fwd", "blockdiag_attn_bwd",
            "blockdiag_mark_main_kernel", "blockdiag_last_error", "blockdiag_version")
+
+
+class MetaDesc(ctypes.Structure):
+    """``bd_meta``: host descriptor of a device metadata buffer, filled by
+    ``blockdiag_meta_build`` / ``blockdiag_meta_build_host`` with the sizes
+    the buffer was built for (the attention calls check them)."""
+    _fields_ = [("magic", ctypes.c_uint32), ("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("row_offset", ctypes.c_int32), ("q_len", ctypes.c_int32), ("n_seg", ctypes.c_int32),
+                ("n_ints", ctypes.c_uint64), ("data", ctypes.c_void_p)]
+
+
+META_MAGIC = 0x54454D42
 
 
 class BlockdiagError(RuntimeError):
@@ -78,19 +90,20 @@ def load_library():
     lib.blockdiag_validate.restype = ctypes.c_int
     lib.blockdiag_meta_ints.argtypes = [i32, i32, i32]
     lib.blockdiag_meta_ints.restype = sz
-    lib.blockdiag_meta_build.argtypes = [p, i32, i32, i32, i32, i32, p, p]
+    pdesc = ctypes.POINTER(MetaDesc)
+    lib.blockdiag_meta_build.argtypes = [p, i32, i32, i32, i32, i32, p, sz, pdesc, p]
     lib.blockdiag_meta_build.restype = ctypes.c_int
-    lib.blockdiag_meta_build_host.argtypes = [pi32, i32, i32, i32, i32, i32, p, p]
+    lib.blockdiag_meta_build_host.argtypes = [pi32, i32, i32, i32, i32, i32, p, sz, pdesc, p]
     lib.blockdiag_meta_build_host.restype = ctypes.c_int
     lib.blockdiag_meta_inline_max_seg.argtypes = []
     lib.blockdiag_meta_inline_max_seg.restype = i32
     lib.blockdiag_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, i32, i32, i32]
     lib.blockdiag_workspace_bytes.restype = sz
     lib.blockdiag_attn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
-                                       p, p, p, p, p, p, p, sz, p]
+                                       p, p, p, pdesc, p, p, p, sz, p]
     lib.blockdiag_attn_fwd.restype = ctypes.c_int
     lib.blockdiag_attn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
-                                       p, p, p, p, p, p, p, p, p, p, p, sz, p]
+                                       p, p, p, p, p, p, pdesc, p, p, p, p, sz, p]
     lib.blockdiag_attn_bwd.restype = ctypes.c_int
     lib.blockdiag_mark_main_kernel.argtypes = [p, p]
     lib.blockdiag_mark_main_kernel.restype = ctypes.c_int
@@ -118,8 +131,10 @@ class SegTable:
 
     Host arrays (numpy int32): ``cu_q``, ``cu_k`` ([n_seg + 1]) and ``k_begin``
     ([n_seg]) as defined in include/blockdiag.h.  With a device, ``table``
-    holds their concatenation on the device and ``meta`` the per-row and
-    per-key mask bounds built from it by ``blockdiag_meta_build``."""
+    holds their concatenation on the device, ``meta`` the per-row and
+    per-key mask bounds built from it by ``blockdiag_meta_build`` and
+    ``desc`` the buffer's descriptor (``bd_meta``) that the attention calls
+    take."""
     batch: int
     seq_len: int
     row_offset: int
@@ -132,6 +147,7 @@ class SegTable:
     max_k: int
     table: object = None
     meta: object = None
+    desc: object = None
     _pinned: object = None
 
     def to(self, device, inline=None):
@@ -145,19 +161,22 @@ class SegTable:
         flat = np.ascontiguousarray(np.concatenate([self.cu_q, self.cu_k, self.k_begin]), dtype=np.int32)
         n_meta = lib.blockdiag_meta_ints(self.batch, self.seq_len, self.q_len)
         meta = torch.empty(max(int(n_meta), 1), dtype=torch.int32, device=device)
+        desc = MetaDesc()
         stream = torch.cuda.current_stream(meta.device).cuda_stream
         if inline is None:
             inline = self.n_seg <= lib.blockdiag_meta_inline_max_seg()
         with torch.cuda.device(meta.device):  # the library launches on the current device
             if inline:
                 _check(lib.blockdiag_meta_build_host(_ptr(flat), self.n_seg, self.batch, self.seq_len,
-                                                     self.row_offset, self.q_len, meta.data_ptr(), stream))
-                return dataclasses.replace(self, table=None, meta=meta, _pinned=None)
+                                                     self.row_offset, self.q_len, meta.data_ptr(), meta.numel(),
+                                                     ctypes.byref(desc), stream))
+                return dataclasses.replace(self, table=None, meta=meta, desc=desc, _pinned=None)
             pinned = torch.from_numpy(flat).pin_memory()
             table = pinned.to(meta.device, non_blocking=True)  # no host sync; pinned copy kept alive below
             _check(lib.blockdiag_meta_build(table.data_ptr(), self.n_seg, self.batch, self.seq_len,
-                                            self.row_offset, self.q_len, meta.data_ptr(), stream))
-        return dataclasses.replace(self, table=table, meta=meta, _pinned=pinned)
+                                            self.row_offset, self.q_len, meta.data_ptr(), meta.numel(),
+                                            ctypes.byref(desc), stream))
+        return dataclasses.replace(self, table=table, meta=meta, desc=desc, _pinned=pinned)
 
     def q_order(self):
         """(order, stats) views of the device metadata: the launch order of
@@ -276,7 +295,7 @@ def _shapes(q, k, v, seg):
     for t in (q, k, v):
         if not t.is_contiguous() or t.device != q.device or t.dtype != q.dtype:
             raise BlockdiagError(1, "q, k, v must be contiguous device tensors of one dtype on one device")
-    if seg.meta is None or seg.meta.device != q.device:
+    if seg.meta is None or seg.desc is None or seg.meta.device != q.device:
         raise BlockdiagError(1, "segment table has no device metadata on the tensors' device")
     return B, L, Hq, d, S, Hkv
 
@@ -302,7 +321,7 @@ def attn_fwd(q, k, v, seg, scale=None):
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):  # the library launches on the current device
         _check(lib.blockdiag_attn_fwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(),
-                                      k.data_ptr(), v.data_ptr(), seg.meta.data_ptr(), o.data_ptr(),
+                                      k.data_ptr(), v.data_ptr(), ctypes.byref(seg.desc), o.data_ptr(),
                                       lse.data_ptr(), ws.data_ptr(), ws_bytes, stream))
     return o, lse
 
@@ -329,7 +348,7 @@ def attn_bwd(q, k, v, o, lse, do, seg, scale=None):
     with torch.cuda.device(q.device):  # the library launches on the current device
         _check(lib.blockdiag_attn_bwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(),
                                       k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                      do.data_ptr(), seg.meta.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                      do.data_ptr(), ctypes.byref(seg.desc), dq.data_ptr(), dk.data_ptr(),
                                       dv.data_ptr(), ws.data_ptr(), ws_bytes, stream))
     return dq, dk, dv
 

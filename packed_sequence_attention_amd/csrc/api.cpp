@@ -53,6 +53,56 @@ bool use_mfma_bwd_full(bd_dtype dtype, int32_t seq_len, int32_t q_len, int32_t h
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// O(1) host check that a metadata descriptor was built for this call's sizes
+// (the kernels index the buffer with the call's batch, seq_len and q_len).
+bd_status check_meta(const bd_meta* m, int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len) {
+  if (m == nullptr) return fail(BD_ERR_INVALID_ARG, "null metadata descriptor");
+  if (m->magic != BD_META_MAGIC) return fail(BD_ERR_INVALID_ARG, "metadata descriptor was not built");
+  if (m->batch != batch || m->seq_len != seq_len || m->row_offset != row_offset || m->q_len != q_len)
+    return fail(BD_ERR_INVALID_ARG,
+                "metadata built for batch %d seq_len %d row_offset %d q_len %d, called with %d %d %d %d",
+                m->batch, m->seq_len, m->row_offset, m->q_len, batch, seq_len, row_offset, q_len);
+  const size_t need = blockdiag_meta_ints(batch, seq_len, q_len);
+  if (m->n_ints < need)
+    return fail(BD_ERR_INVALID_ARG, "metadata holds %llu ints, %zu needed",
+                static_cast<unsigned long long>(m->n_ints), need);
+  if (need > 0 && m->data == nullptr) return fail(BD_ERR_INVALID_ARG, "null metadata buffer");
+  return BD_OK;
+}
+
+// Shared argument checks of the two metadata builders; clears *desc first.
+bd_status check_meta_build(const int32_t* table, int32_t n_seg, int32_t batch, int32_t seq_len,
+                           int32_t row_offset, int32_t q_len, int32_t* d_meta, size_t capacity,
+                           bd_meta* desc) {
+  if (desc == nullptr) return fail(BD_ERR_INVALID_ARG, "null descriptor");
+  desc->magic = 0;
+  if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0 || n_seg < 0)
+    return fail(BD_ERR_INVALID_ARG, "negative size");
+  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
+    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
+  if (static_cast<int64_t>(batch) * seq_len > kMaxElems) return fail(BD_ERR_INVALID_ARG, "too large");
+  const size_t need = blockdiag_meta_ints(batch, seq_len, q_len);
+  if (need > 0) {
+    if (table == nullptr || d_meta == nullptr) return fail(BD_ERR_INVALID_ARG, "null pointer");
+    if (capacity < need) return fail(BD_ERR_CAPACITY, "metadata buffer holds %zu ints, %zu needed", capacity, need);
+    if (n_seg == 0 && static_cast<int64_t>(batch) * q_len > 0)
+      return fail(BD_ERR_BAD_METADATA, "empty segment table for a non-empty chunk");
+  }
+  return BD_OK;
+}
+
+void fill_desc(bd_meta* desc, int32_t n_seg, int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len,
+               const int32_t* d_meta) {
+  desc->batch = batch;
+  desc->seq_len = seq_len;
+  desc->row_offset = row_offset;
+  desc->q_len = q_len;
+  desc->n_seg = n_seg;
+  desc->n_ints = blockdiag_meta_ints(batch, seq_len, q_len);
+  desc->data = d_meta;
+  desc->magic = BD_META_MAGIC;
+}
+
 thread_local hipEvent_t g_mark_start = nullptr;
 thread_local hipEvent_t g_mark_stop = nullptr;
 
@@ -83,20 +133,17 @@ extern "C" size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_
 
 extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, int32_t n_seg, int32_t batch,
                                           int32_t seq_len, int32_t row_offset, int32_t q_len,
-                                          int32_t* d_meta, void* stream) {
+                                          int32_t* d_meta, size_t meta_capacity, bd_meta* desc,
+                                          void* stream) {
   bd::clear_error();
-  if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0 || n_seg < 0)
-    return fail(BD_ERR_INVALID_ARG, "negative size");
-  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
-    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
-  if (static_cast<int64_t>(batch) * seq_len > kMaxElems) return fail(BD_ERR_INVALID_ARG, "too large");
-  if (blockdiag_meta_ints(batch, seq_len, q_len) == 0) return BD_OK;
-  if (d_table == nullptr || d_meta == nullptr) return fail(BD_ERR_INVALID_ARG, "null pointer");
-  if (n_seg == 0 && static_cast<int64_t>(batch) * q_len > 0)
-    return fail(BD_ERR_BAD_METADATA, "empty segment table for a non-empty chunk");
-  hipError_t e = bd::launch_meta_build(d_table, false, n_seg, batch, seq_len, row_offset, q_len, d_meta,
-                                       static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
+  bd_status st = check_meta_build(d_table, n_seg, batch, seq_len, row_offset, q_len, d_meta, meta_capacity, desc);
+  if (st != BD_OK) return st;
+  if (blockdiag_meta_ints(batch, seq_len, q_len) > 0) {
+    hipError_t e = bd::launch_meta_build(d_table, false, n_seg, batch, seq_len, row_offset, q_len, d_meta,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
+  }
+  fill_desc(desc, n_seg, batch, seq_len, row_offset, q_len, d_meta);
   return BD_OK;
 }
 
@@ -104,23 +151,20 @@ extern "C" int32_t blockdiag_meta_inline_max_seg(void) { return bd::kInlineSeg; 
 
 extern "C" bd_status blockdiag_meta_build_host(const int32_t* h_table, int32_t n_seg, int32_t batch,
                                                int32_t seq_len, int32_t row_offset, int32_t q_len,
-                                               int32_t* d_meta, void* stream) {
+                                               int32_t* d_meta, size_t meta_capacity, bd_meta* desc,
+                                               void* stream) {
   bd::clear_error();
-  if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0 || n_seg < 0)
-    return fail(BD_ERR_INVALID_ARG, "negative size");
-  if (static_cast<int64_t>(row_offset) + q_len > seq_len)
-    return fail(BD_ERR_INVALID_ARG, "row_offset + q_len > seq_len");
-  if (static_cast<int64_t>(batch) * seq_len > kMaxElems) return fail(BD_ERR_INVALID_ARG, "too large");
+  bd_status st = check_meta_build(h_table, n_seg, batch, seq_len, row_offset, q_len, d_meta, meta_capacity, desc);
+  if (st != BD_OK) return st;
   if (n_seg > bd::kInlineSeg)
     return fail(BD_ERR_CAPACITY, "%d segments: at most %d pass by value (use blockdiag_meta_build)", n_seg,
                 bd::kInlineSeg);
-  if (blockdiag_meta_ints(batch, seq_len, q_len) == 0) return BD_OK;
-  if (h_table == nullptr || d_meta == nullptr) return fail(BD_ERR_INVALID_ARG, "null pointer");
-  if (n_seg == 0 && static_cast<int64_t>(batch) * q_len > 0)
-    return fail(BD_ERR_BAD_METADATA, "empty segment table for a non-empty chunk");
-  hipError_t e = bd::launch_meta_build(h_table, true, n_seg, batch, seq_len, row_offset, q_len, d_meta,
-                                       static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
+  if (blockdiag_meta_ints(batch, seq_len, q_len) > 0) {
+    hipError_t e = bd::launch_meta_build(h_table, true, n_seg, batch, seq_len, row_offset, q_len, d_meta,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
+  }
+  fill_desc(desc, n_seg, batch, seq_len, row_offset, q_len, d_meta);
   return BD_OK;
 }
 
@@ -135,18 +179,20 @@ extern "C" size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t 
 extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
                                         int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
                                         float scale, const void* q, const void* k, const void* v,
-                                        const int32_t* d_meta, void* o, float* lse, void* workspace,
+                                        const bd_meta* meta, void* o, float* lse, void* workspace,
                                         size_t workspace_bytes, void* stream) {
   bd::clear_error();
   (void)workspace;
   bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale);
   if (st != BD_OK) return st;
   if (batch == 0 || q_len == 0) return BD_OK;
-  if (!q || !k || !v || !d_meta || !o || !lse) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
+  if (!q || !k || !v || !o || !lse) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
+  st = check_meta(meta, batch, seq_len, row_offset, q_len);
+  if (st != BD_OK) return st;
   const size_t need = blockdiag_workspace_bytes(0, dtype, batch, seq_len, q_len, h_q, h_kv, head_dim);
   if (workspace_bytes < need) return fail(BD_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   bd::FwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
-                q, k, v, d_meta, o, lse, nullptr, nullptr};
+                q, k, v, meta->data, o, lse, nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma_fwd(dtype, seq_len, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
@@ -159,13 +205,13 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
                                         int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
                                         float scale, const void* q, const void* k, const void* v,
                                         const void* o, const float* lse, const void* d_o,
-                                        const int32_t* d_meta, void* dq, void* dk, void* dv,
+                                        const bd_meta* meta, void* dq, void* dk, void* dv,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   bd::clear_error();
   bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale);
   if (st != BD_OK) return st;
   if (batch == 0) return BD_OK;
-  if (!k || !v || !d_meta || !dk || !dv) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
+  if (!k || !v || !dk || !dv) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
   if (q_len > 0 && (!q || !o || !lse || !d_o || !dq)) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
   const size_t need = blockdiag_workspace_bytes(1, dtype, batch, seq_len, q_len, h_q, h_kv, head_dim);
   if (workspace_bytes < need) return fail(BD_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
@@ -179,9 +225,11 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
     if (e != hipSuccess) return fail(BD_ERR_HIP, "zero-fill: %s", hipGetErrorString(e));
     return BD_OK;
   }
+  st = check_meta(meta, batch, seq_len, row_offset, q_len);
+  if (st != BD_OK) return st;
   const bool mf = use_mfma_bwd_full(dtype, seq_len, q_len, head_dim, h_q, h_kv, scale);
   bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
-                q, k, v, o, lse, d_o, d_meta, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
+                q, k, v, o, lse, d_o, meta->data, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

@@ -230,6 +230,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     sRed[kgrp] = wqlo;
     sRed[2 + kgrp] = wqhi;
   }
+  // The early tile is written into LDS by direct loads that another wave
+  // reads: wait for every load of this wave (the early tile's, and the V
+  // loads behind the LDS stores above) before the barrier publishes them.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int gqlo = min(sRed[0], sRed[1]);
   const int gqhi = max(sRed[2], sRed[3]);
@@ -272,8 +276,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // a wave's own H2 orders its group's loads and reads.
   const bool late = hsub >= 2;
   if (n_it > 0) {
-    // The early tile landed before the barrier above (its fence waits for
-    // every load); it is reloaded only if the metadata disagrees.
+    // The early tile landed before the barrier above (the explicit wait
+    // before it); it is reloaded only if the metadata disagrees.
     if (!early || qt0 != qt0e) {
       issue_loads(0, 0);
       __builtin_amdgcn_s_waitcnt(0);

@@ -390,18 +390,4 @@ hipError_t launch_zero_u16(void* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t st) {
-  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
-  const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
-  const int lpr = lanes_per_row(a.head_dim);
-  const unsigned grid = static_cast<unsigned>((rows * lpr + 255) / 256);
-  if (a.dtype == 0)
-    bwd_prep_kernel<float><<<grid, 256, 0, st>>>(s, static_cast<const float*>(a.o),
-                                                 static_cast<const float*>(a.d_o), a.lse, a.rowstat, lpr);
-  else
-    bwd_prep_kernel<uint16_t><<<grid, 256, 0, st>>>(s, static_cast<const uint16_t*>(a.o),
-                                                    static_cast<const uint16_t*>(a.d_o), a.lse, a.rowstat, lpr);
-  return hipGetLastError();
-}
-
 }  // namespace bd

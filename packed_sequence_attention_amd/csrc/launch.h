@@ -80,10 +80,6 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv256(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv64(const BwdArgs& a, hipStream_t stream);
 
-// Backward row statistics: rowstat = (lse * log2(e), delta = rowsum(dO * O)),
-// float32.
-hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);
-
 // Fill n 16-bit words with zeros (a kernel, so it is safe under graph capture).
 hipError_t launch_zero_u16(void* p, int64_t n, hipStream_t stream);
 

@@ -56,6 +56,9 @@ extern "C" bd_status blockdiag_validate(const int32_t* cu_q, const int32_t* cu_k
   if (cu_q == nullptr || cu_k == nullptr || (n > 0 && kb == nullptr))
     return fail(BD_ERR_INVALID_ARG, "null table pointer");
   const int64_t rows = static_cast<int64_t>(batch) * q_len;
+  // An empty chunk has no segments; rejecting any here also keeps the
+  // row-of-segment division below away from q_len = 0.
+  if (n > 0 && rows == 0) return fail(BD_ERR_BAD_METADATA, "%d segments for an empty chunk", n);
   if (cu_q[0] != 0 || cu_k[0] != 0) return fail(BD_ERR_BAD_METADATA, "cu_seqlens must start at 0");
   if (cu_q[n] != rows)
     return fail(BD_ERR_BAD_METADATA, "terminal cu_seqlens_q %d != batch * q_len %lld", cu_q[n],

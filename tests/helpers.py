@@ -102,3 +102,35 @@ def small_case(i, dtype, doc_lens, seq_len, row_offset, q_len, h_q, h_kv, d, sca
     w = synthetic.custom_workload(1000 + i, dtype, doc_lens, seq_len, row_offset, q_len, h_q, h_kv, d,
                                   scale, name=f"case{i}")
     return w, synthetic.draw_tensors(w)
+
+
+def per_doc_grad_errors(w, gpu, ref, heads=None, kv_heads=None):
+    """Worst per-document relative Frobenius error of dQ (the document's rows
+    in the chunk, all query heads) and of dK, dV (the document's keys that
+    the chunk attends, all K/V heads), over every batch row and document: an
+    error confined to a few short documents is not diluted by the others.
+    Keys no chunk row attends must be exactly zero.  ``heads`` / ``kv_heads``
+    select the head slices the arrays hold (default: all)."""
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    r0, r1 = w.row_offset, w.row_offset + w.q_len
+    for b, lens in enumerate(w.doc_lens):
+        for name in ("dk", "dv"):  # keys after the chunk's last row: never attended
+            assert not np.any(gpu[name][b, r1:]), f"{name} nonzero at keys past the chunk"
+        pos = 0
+        for Ln in lens:
+            s, e = pos, pos + Ln
+            pos = e
+            if Ln == 0:
+                continue
+            qa, qb = max(s, r0) - r0, min(e, r1) - r0
+            if qb <= qa:  # no row of the chunk in this document: its keys are unattended
+                for name in ("dk", "dv"):
+                    assert not np.any(gpu[name][b, s:e]), f"{name} nonzero at unattended keys [{s},{e})"
+                continue
+            for name, x, r in (("dq", gpu["dq"][b, qa:qb], ref["dq"][b, qa:qb]),
+                               ("dk", gpu["dk"][b, s:min(e, r1)], ref["dk"][b, s:min(e, r1)]),
+                               ("dv", gpu["dv"][b, s:min(e, r1)], ref["dv"][b, s:min(e, r1)])):
+                den = np.linalg.norm(r)
+                if den > 0:
+                    worst[name] = max(worst[name], float(np.linalg.norm(x - r) / den))
+    return worst

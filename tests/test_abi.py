@@ -3,6 +3,7 @@ include/blockdiag.h declares; the host segmenter is bit-exact against the
 oracle's reference table; the validator rejects malformed tables; the
 attention entry points reject bad arguments before launching anything.
 (No kernel is launched here.)"""
+import ctypes
 import os
 import re
 
@@ -129,6 +130,12 @@ def test_validate_accepts_and_rejects():
         with pytest.raises(bd.BlockdiagError) as e:
             bd.validate(cq, ck, kb, *args)
         assert e.value.code == 2
+    # segments for an empty chunk (q_len = 0, or batch = 0): rejected before
+    # any per-segment arithmetic divides by q_len
+    for dims in ((1, 8, 0, 0), (0, 8, 0, 4)):
+        with pytest.raises(bd.BlockdiagError) as e:
+            bd.validate([0, 5, 0], [0, 5, 0], [0, 0], *dims)
+        assert e.value.code == 2
     # padding segment must end the chunk and start at its first row
     t = bd.segment([[3, 4], [6, 4]], 10, 4, 4)
     bd.validate(t.cu_q, t.cu_k, t.k_begin, 2, 10, 4, 4)
@@ -162,10 +169,17 @@ def test_attention_entry_points_reject_before_launch():
     ws = lib.blockdiag_workspace_bytes(1, 1, 1, 64, 64, 4, 4, 64)
     assert ws > 0
     p = 16  # a non-null dummy value; never dereferenced because the check fails first
-    assert bwd(1, 1, 64, 0, 64, 4, 4, 64, 0.125, *([p] * 10), p, ws - 1, N) == 4
+    m = _desc(1, 64, 0, 64)
+    assert bwd(1, 1, 64, 0, 64, 4, 4, 64, 0.125, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws - 1, N) == 4
     assert b"workspace" in lib.blockdiag_last_error()
     # metadata build rejects an empty table for a non-empty chunk
-    assert lib.blockdiag_meta_build(p, 0, 1, 64, 0, 64, p, N) == 2
+    desc = bd.MetaDesc()
+    cap = lib.blockdiag_meta_ints(1, 64, 64)
+    assert lib.blockdiag_meta_build(p, 0, 1, 64, 0, 64, p, cap, ctypes.byref(desc), N) == 2
+    assert desc.magic == 0
+    # ... a metadata buffer smaller than blockdiag_meta_ints, and a missing descriptor
+    assert lib.blockdiag_meta_build(p, 1, 1, 64, 0, 64, p, cap - 1, ctypes.byref(desc), N) == 3
+    assert lib.blockdiag_meta_build(p, 1, 1, 64, 0, 64, p, cap, None, N) == 1
     # bounds of rows and keys, then the order of the 32-row query tiles and its two statistics
     assert lib.blockdiag_meta_ints(2, 100, 40) == 2 * 2 * 40 + 2 * 2 * 100 + 2 * 2 + 2
 
@@ -179,17 +193,62 @@ def test_meta_build_host_rejects_before_launch():
     assert mx >= 64
     table = np.zeros(3 * (mx + 1) + 2, np.int32)
     p = 16  # non-null dummy device pointer; never dereferenced because the check fails first
+    cap = lib.blockdiag_meta_ints(1, 64, 64)
+    desc = bd.MetaDesc()
+    d = ctypes.byref(desc)
     # one segment over the limit: capacity error, the caller falls back to the device copy
-    assert lib.blockdiag_meta_build_host(bd._ptr(table), mx + 1, 1, 64, 0, 64, p, N) == 3
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), mx + 1, 1, 64, 0, 64, p, cap, d, N) == 3
     assert b"segments" in lib.blockdiag_last_error()
     # empty table for a non-empty chunk; negative sizes; chunk out of range; null pointers
-    assert lib.blockdiag_meta_build_host(bd._ptr(table), 0, 1, 64, 0, 64, p, N) == 2
-    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, -1, 64, 0, 64, p, N) == 1
-    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, 1, 64, 32, 64, p, N) == 1
-    assert lib.blockdiag_meta_build_host(N, 1, 1, 64, 0, 64, p, N) == 1
-    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, 1, 64, 0, 64, N, N) == 1
-    # nothing to build is a no-op
-    assert lib.blockdiag_meta_build_host(N, 0, 0, 0, 0, 0, N, N) == 0
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 0, 1, 64, 0, 64, p, cap, d, N) == 2
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, -1, 64, 0, 64, p, cap, d, N) == 1
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, 1, 64, 32, 64, p, cap, d, N) == 1
+    assert lib.blockdiag_meta_build_host(N, 1, 1, 64, 0, 64, p, cap, d, N) == 1
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, 1, 64, 0, 64, N, cap, d, N) == 1
+    # metadata buffer too small for the sizes
+    assert lib.blockdiag_meta_build_host(bd._ptr(table), 1, 1, 64, 0, 64, p, cap - 1, d, N) == 3
+    assert desc.magic == 0
+    # nothing to build is a no-op that still describes the (empty) buffer
+    assert lib.blockdiag_meta_build_host(N, 0, 0, 0, 0, 0, N, 0, d, N) == 0
+    assert desc.magic == bd.META_MAGIC and desc.n_ints == 0
+
+
+def _desc(batch, seq_len, row_offset, q_len, n_ints=None, magic=None, data=16):
+    lib = bd.load_library()
+    m = bd.MetaDesc()
+    m.magic = bd.META_MAGIC if magic is None else magic
+    m.batch, m.seq_len, m.row_offset, m.q_len = batch, seq_len, row_offset, q_len
+    m.n_seg = 1
+    m.n_ints = lib.blockdiag_meta_ints(batch, seq_len, q_len) if n_ints is None else n_ints
+    m.data = data
+    return m
+
+
+def test_attention_rejects_metadata_built_for_other_sizes():
+    """The kernels index the metadata with the call's own sizes, so a
+    descriptor built for another chunk (smaller q_len, other row_offset or
+    seq_len), a descriptor that was never built, one whose buffer is too
+    small and a missing one are all rejected on the host with
+    BD_ERR_INVALID_ARG before anything is launched (every tensor pointer
+    below is a dummy that a launch would fault on)."""
+    lib = bd.load_library()
+    p = 16
+    args = (1, 2, 256, 64, 128, 8, 2, 64, 0.125)  # bf16, B=2, S=256, chunk [64, 192)
+    ws = lib.blockdiag_workspace_bytes(1, 1, 2, 256, 128, 8, 2, 64)
+    bad = [_desc(2, 256, 64, 64),                  # built for a smaller chunk
+           _desc(2, 256, 0, 128),                  # other row_offset
+           _desc(2, 128, 0, 128),                  # other seq_len
+           _desc(1, 256, 64, 128),                 # other batch
+           _desc(2, 256, 64, 128, magic=0),        # never built
+           _desc(2, 256, 64, 128, n_ints=100),     # buffer smaller than the sizes need
+           _desc(2, 256, 64, 128, data=None)]      # no buffer
+    for m in bad:
+        assert lib.blockdiag_attn_fwd(*args, p, p, p, ctypes.byref(m), p, p, p, 0, None) == 1
+        assert b"metadata" in lib.blockdiag_last_error()
+        assert lib.blockdiag_attn_bwd(*args, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws, None) == 1
+        assert b"metadata" in lib.blockdiag_last_error()
+    assert lib.blockdiag_attn_fwd(*args, p, p, p, None, p, p, p, 0, None) == 1
+    assert lib.blockdiag_attn_bwd(*args, p, p, p, p, p, p, None, p, p, p, p, ws, None) == 1
 
 
 def test_doc_lens_from_ids():
