@@ -273,6 +273,30 @@ bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * blockdiag_attn_bwd_noalloc -- blockdiag_attn_bwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, which is replaced by a static device array of
+ * blockdiag_noalloc_scratch_bytes() bytes (16 MiB) that the library holds on
+ * every GPU it runs on until the process ends.  The array holds the float32
+ * row statistics (8 bytes per local row and query head), so
+ * batch * q_len * h_q may be at most 2^21; larger calls return
+ * BD_ERR_WORKSPACE before anything is launched.  The call allocates
+ * nothing; its first call on a device looks up that device's copy of the
+ * array (the caller's current device).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams, threads)
+ * race and give wrong results; calls ordered on one stream are safe.
+ * Results are those of blockdiag_attn_bwd, bit for bit.
+ */
+size_t blockdiag_noalloc_scratch_bytes(void);
+bd_status blockdiag_attn_bwd_noalloc(bd_dtype dtype, int32_t batch, int32_t seq_len,
+                                     int32_t row_offset, int32_t q_len, int32_t h_q, int32_t h_kv,
+                                     int32_t head_dim, float scale, const void *q, const void *k,
+                                     const void *v, const void *o, const float *lse,
+                                     const void *d_o, const bd_meta *meta, void *dq, void *dk,
+                                     void *dv, void *stream);
+
+/*
  * blockdiag_mark_main_kernel -- profiling hook.  The next blockdiag_attn_fwd
  * or blockdiag_attn_bwd call made on this thread records start_event on its
  * stream right before launching its main attention kernel and stop_event

@@ -47,6 +47,7 @@ STATUS = {0: "BD_OK", 1: "BD_ERR_INVALID_ARG", 2: "BD_ERR_BAD_METADATA", 3: "BD_
 EXPORTS = ("blockdiag_segment", "blockdiag_validate", "blockdiag_meta_ints", "blockdiag_meta_build",
            "blockdiag_meta_build_host", "blockdiag_meta_inline_max_seg",
            "blockdiag_workspace_bytes", "blockdiag_attn_fwd", "blockdiag_attn_bwd",
+           "blockdiag_attn_bwd_noalloc", "blockdiag_noalloc_scratch_bytes",
            "blockdiag_mark_main_kernel", "blockdiag_last_error", "blockdiag_version")
 
 
@@ -105,6 +106,11 @@ def load_library():
     lib.blockdiag_attn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                        p, p, p, p, p, p, pdesc, p, p, p, p, sz, p]
     lib.blockdiag_attn_bwd.restype = ctypes.c_int
+    lib.blockdiag_attn_bwd_noalloc.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                               p, p, p, p, p, p, pdesc, p, p, p, p]
+    lib.blockdiag_attn_bwd_noalloc.restype = ctypes.c_int
+    lib.blockdiag_noalloc_scratch_bytes.argtypes = []
+    lib.blockdiag_noalloc_scratch_bytes.restype = sz
     lib.blockdiag_mark_main_kernel.argtypes = [p, p]
     lib.blockdiag_mark_main_kernel.restype = ctypes.c_int
     lib.blockdiag_last_error.argtypes = []
