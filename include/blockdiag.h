@@ -32,7 +32,11 @@
  *     synchronisation.
  *   - Tensors are dense, row-major, contiguous:
  *       q, o, dO, dq : [batch][q_len][h_q][head_dim]
- *       k, v, dk, dv : [batch][seq_len][h_kv][head_dim]   (whole packed row)
+ *       k, v, dk, dv : [batch][kv_len][h_kv][head_dim]: keys
+ *                      [kv_begin, kv_begin + kv_len) of every row -- the
+ *                      whole packed row (kv_begin = 0, kv_len = seq_len) or
+ *                      a window holding every key the chunk attends (Summary
+ *                      and Design overview, exchange.py: needed-only K/V)
  *       lse          : [batch][h_q][q_len] float32, natural log of the softmax
  *                      denominator in units of scaled logits; -inf on rows
  *                      that attend no key (padding)
@@ -123,6 +127,56 @@ bd_status blockdiag_validate(const int32_t *cu_seqlens_q, const int32_t *cu_seql
                              int32_t seq_len, int32_t row_offset, int32_t q_len);
 
 /*
+ * blockdiag_kv_plan -- needed-only K/V exchange plan of one context-parallel
+ * rank (host only, integer only).  Summary: instead of all-gathering the
+ * whole row's K/V, a rank can receive only the keys its rows attend -- from
+ * its left neighbour (halo p2p), or with an all-to-all-v when a document
+ * spans more than two ranks -- which cuts its K/V from the whole row to its
+ * own chunk plus the straddling prefix; Design overview, batch.py (rows
+ * padded to a multiple of cp, contiguous slice per rank) and exchange.py;
+ * Proof: the plan geometry is checked on the CPU.
+ *
+ * Rank r of cp holds rows [r * S/cp, (r + 1) * S/cp) of every batch row
+ * (seq_len must be a multiple of cp).  Its rows of batch row b attend the
+ * keys [doc_start(r0), min(r1, end of the row's documents)) -- empty when
+ * r0 is padding -- and the part left of r0 is the halo, owned by lower
+ * ranks.
+ * Inputs (host): doc_lens / docs_per_row / batch / seq_len as for
+ *   blockdiag_segment; cp >= 1; 0 <= rank < cp; align >= 1.
+ * Outputs (host):
+ *   *kv_begin, *kv_end  the rank's K/V window [kv_begin, kv_end) for
+ *       blockdiag_attn_fwd / _bwd: kv_end = r1, kv_begin = the smallest key
+ *       any of its rows attends (at most r0), rounded down to a multiple of
+ *       align (64 for the attention calls).  Keys of the window that are not
+ *       in a row's receive ranges or own chunk are never attended by that
+ *       row; the caller zero-fills them.
+ *   recv[*n_recv]  ranges (row, peer, begin, end): keys [begin, end) of batch
+ *       row `row` that this rank receives from rank `peer` (exactly the halo,
+ *       split by owning rank, rows in order, lower ranks first).
+ *   send[*n_send]  ranges this rank sends: keys [begin, end) of its own chunk
+ *       that rank `peer` > rank attends (rows in order, peers ascending).
+ *   *rank_mode  0: no halo; 1: every received key comes from rank - 1 (halo
+ *       p2p); 2: some come from a rank further left (all-to-all-v).
+ *   *step_mode  the largest rank_mode over all ranks: the exchange every
+ *       rank of the step runs (0 none, 1 halo, 2 all-to-all-v), so no rank
+ *       takes a different collective.
+ * Errors: BD_ERR_INVALID_ARG, BD_ERR_BAD_METADATA (negative length, row sum
+ * > seq_len), BD_ERR_CAPACITY (*n_recv / *n_send hold the counts needed;
+ * the range arrays may then be partly written).
+ */
+typedef struct bd_kv_range {
+  int32_t row;    /* batch row                     */
+  int32_t peer;   /* the other rank                */
+  int32_t begin;  /* first key position (in row)   */
+  int32_t end;    /* one past the last             */
+} bd_kv_range;
+bd_status blockdiag_kv_plan(const int32_t *doc_lens, const int32_t *docs_per_row, int32_t batch,
+                            int32_t seq_len, int32_t cp, int32_t rank, int32_t align,
+                            int32_t *kv_begin, int32_t *kv_end, int32_t capacity,
+                            bd_kv_range *recv, int32_t *n_recv, bd_kv_range *send,
+                            int32_t *n_send, int32_t *rank_mode, int32_t *step_mode);
+
+/*
  * bd_meta -- host descriptor of a device metadata buffer.  It records the
  * sizes the buffer was built for, so the attention calls can check in O(1)
  * on the host that the metadata matches their own sizes before anything is
@@ -141,6 +195,9 @@ typedef struct bd_meta {
   int32_t row_offset;
   int32_t q_len;
   int32_t n_seg;        /* segments of the table it was built from         */
+  int32_t kv_lo;        /* keys the chunk attends, over all batch rows:    */
+  int32_t kv_hi;        /*   [kv_lo, kv_hi) (kv_lo = 0 when unknown)       */
+  int32_t reserved;
   uint64_t n_ints;      /* int32 entries written: blockdiag_meta_ints(...) */
   const int32_t *data;  /* the device buffer (caller-owned)                */
 } bd_meta;
@@ -181,14 +238,19 @@ typedef struct bd_meta {
  *               the order.
  *   desc      (host, required) receives the buffer's descriptor for the
  *             attention calls; on any error its magic is set to 0.
+ *   h_table   (host, optional) the same table in host memory: the
+ *             descriptor then records the key window the chunk attends
+ *             (kv_lo, kv_hi), which a window-only K/V call is checked
+ *             against.  NULL records kv_lo = 0, kv_hi = row_offset + q_len,
+ *             so only K/V windows starting at key 0 are accepted.
  * The table is not re-validated here (that needs a sync); the kernel clamps
  * every bound to its row so a corrupt table cannot make later kernels read
  * out of bounds.  Errors: BD_ERR_INVALID_ARG, BD_ERR_CAPACITY (meta_capacity
  * too small; nothing is launched), BD_ERR_HIP.
  */
 size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_len);
-bd_status blockdiag_meta_build(const int32_t *d_table, int32_t n_seg, int32_t batch,
-                               int32_t seq_len, int32_t row_offset, int32_t q_len,
+bd_status blockdiag_meta_build(const int32_t *d_table, const int32_t *h_table, int32_t n_seg,
+                               int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len,
                                int32_t *d_meta, size_t meta_capacity, bd_meta *desc,
                                void *stream);
 
@@ -199,8 +261,8 @@ bd_status blockdiag_meta_build(const int32_t *d_table, int32_t n_seg, int32_t ba
  * during the call and travels to the kernel in its launch arguments, so the
  * step needs no host-to-device copy of it (Summary: per-step precompute,
  * zero per-layer host syncs).  h_table is not retained after the call
- * returns.  d_meta, meta_capacity, desc, the output and the stream ordering
- * are as for blockdiag_meta_build.  Errors: BD_ERR_CAPACITY when n_seg
+ * returns.  d_meta, meta_capacity, desc (with the key window recorded), the
+ * output and the stream ordering are as for blockdiag_meta_build.  Errors: BD_ERR_CAPACITY when n_seg
  * exceeds the limit (use blockdiag_meta_build) or meta_capacity is too
  * small (nothing is launched), BD_ERR_INVALID_ARG, BD_ERR_BAD_METADATA,
  * BD_ERR_HIP.
@@ -221,6 +283,15 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
 /*
  * blockdiag_attn_fwd -- O and LSE of the chunk (Summary: the varlen kernel;
  * Design overview, runtime.py: drop-in SDPA; packed.py: row_offset = 0).
+ *   kv_begin, kv_len: the K/V window held by k and v (whole row: 0 and
+ *   seq_len).  kv_begin must be a multiple of 64, at most the first key the
+ *   chunk attends (the descriptor's kv_lo) and at most row_offset; the
+ *   window must reach the chunk's end: row_offset + q_len <= kv_begin +
+ *   kv_len <= seq_len.  Keys of the window that a row does not attend are
+ *   read but weighted by exactly zero; they must hold finite values (the
+ *   exchange plan's callers zero-fill them).  Results do not depend on the
+ *   window: O, LSE and dQ are bitwise those of the whole-row call, dK / dV
+ *   bitwise its rows of the window.
  *   q, k, v (device, dtype) as in the conventions above; meta (host) the
  *   descriptor blockdiag_meta_build wrote for the same batch, seq_len,
  *   row_offset and q_len (a descriptor built for other sizes, or not built,
@@ -231,8 +302,8 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
  *   bf16, h_q % h_kv = 0.  bf16 with h_q / h_kv a multiple of 4 runs on the
  *   matrix-core kernels for head_dim 64, 128 and 256 when
  *   one batch row of K (or V), in bytes, stays below 2^31 with one tile of
- *   slack: (seq_len + 32) * h_kv * head_dim * 2 for the forward; the
- *   backward needs (seq_len + 64) * h_kv * head_dim * 2 and
+ *   slack: (kv_len + 32) * h_kv * head_dim * 2 for the forward; the
+ *   backward needs (kv_len + 64) * h_kv * head_dim * 2 and
  *   (q_len + 32) * h_q * head_dim * 2 below 2^31.  Everything else runs on
  *   the generic kernels (64-bit indexing, float32 arithmetic).
  *   bf16 inputs are multiplied on matrix cores with float32 accumulation; the
@@ -242,7 +313,8 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
  * Errors: BD_ERR_INVALID_ARG, BD_ERR_UNSUPPORTED, BD_ERR_WORKSPACE, BD_ERR_HIP.
  */
 bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
-                             int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                             int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
+                             int32_t h_kv, int32_t head_dim,
                              float scale, const void *q, const void *k, const void *v,
                              const bd_meta *meta, void *o, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream);
@@ -253,11 +325,12 @@ bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
  * incoming gradient.  o and lse are the forward's outputs; d_o like o;
  * meta as for blockdiag_attn_fwd (not read, and may be NULL, when q_len or
  * batch is 0).
- *   dq (device, like q) is written in full; dk, dv (device, like k) are
- *   written for every key of every row -- the chunk's partial gradients, zero
- *   at keys no local row attends, so summing them over the chunks of a row
- *   gives the full gradient (Design overview, exchange.py: the K/V gradient
- *   is reduce-scattered with SUM).
+ *   dq (device, like q) is written in full; dk, dv (device, like k: the
+ *   window [kv_begin, kv_begin + kv_len) of every row) are written for every
+ *   key of the window -- the chunk's partial gradients, zero at keys no local
+ *   row attends, so summing them over the chunks of a row gives the full
+ *   gradient (Design overview, exchange.py: the K/V gradient is
+ *   reduce-scattered with SUM, or index-added back for needed-only K/V).
  *   workspace: at least blockdiag_workspace_bytes(1, ...) bytes of device
  *   memory (float32 row statistics: lse * log2(e) and delta = rowsum(dO * O)
  *   per row and query head, 8 bytes each).
@@ -266,7 +339,8 @@ bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
  * Errors: as blockdiag_attn_fwd.
  */
 bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
-                             int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                             int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
+                             int32_t h_kv, int32_t head_dim,
                              float scale, const void *q, const void *k, const void *v,
                              const void *o, const float *lse, const void *d_o,
                              const bd_meta *meta, void *dq, void *dk, void *dv,
@@ -290,7 +364,8 @@ bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
  */
 size_t blockdiag_noalloc_scratch_bytes(void);
 bd_status blockdiag_attn_bwd_noalloc(bd_dtype dtype, int32_t batch, int32_t seq_len,
-                                     int32_t row_offset, int32_t q_len, int32_t h_q, int32_t h_kv,
+                                     int32_t row_offset, int32_t q_len, int32_t kv_begin,
+                                     int32_t kv_len, int32_t h_q, int32_t h_kv,
                                      int32_t head_dim, float scale, const void *q, const void *k,
                                      const void *v, const void *o, const float *lse,
                                      const void *d_o, const bd_meta *meta, void *dq, void *dk,

@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "BlockdiagError", "MetaDesc", "SegTable", "segment", "validate", "doc_lens_from_ids",
-    "attn_fwd", "attn_bwd", "attention", "library_path", "load_library",
+    "attn_fwd", "attn_bwd", "attention", "library_path", "load_library", "KvPlan", "kv_plan",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +44,7 @@ _LIB = None
 
 STATUS = {0: "BD_OK", 1: "BD_ERR_INVALID_ARG", 2: "BD_ERR_BAD_METADATA", 3: "BD_ERR_CAPACITY",
           4: "BD_ERR_WORKSPACE", 5: "BD_ERR_UNSUPPORTED", 6: "BD_ERR_HIP"}
-EXPORTS = ("blockdiag_segment", "blockdiag_validate", "blockdiag_meta_ints", "blockdiag_meta_build",
+EXPORTS = ("blockdiag_segment", "blockdiag_validate", "blockdiag_kv_plan", "blockdiag_meta_ints", "blockdiag_meta_build",
            "blockdiag_meta_build_host", "blockdiag_meta_inline_max_seg",
            "blockdiag_workspace_bytes", "blockdiag_attn_fwd", "blockdiag_attn_bwd",
            "blockdiag_attn_bwd_noalloc", "blockdiag_noalloc_scratch_bytes",
@@ -57,7 +57,15 @@ class MetaDesc(ctypes.Structure):
     the buffer was built for (the attention calls check them)."""
     _fields_ = [("magic", ctypes.c_uint32), ("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("row_offset", ctypes.c_int32), ("q_len", ctypes.c_int32), ("n_seg", ctypes.c_int32),
+                ("kv_lo", ctypes.c_int32), ("kv_hi", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("n_ints", ctypes.c_uint64), ("data", ctypes.c_void_p)]
+
+
+class KvRange(ctypes.Structure):
+    """``bd_kv_range``: keys [begin, end) of batch row ``row`` exchanged with
+    rank ``peer``."""
+    _fields_ = [("row", ctypes.c_int32), ("peer", ctypes.c_int32), ("begin", ctypes.c_int32),
+                ("end", ctypes.c_int32)]
 
 
 META_MAGIC = 0x54454D42
@@ -89,10 +97,14 @@ def load_library():
     lib.blockdiag_segment.restype = ctypes.c_int
     lib.blockdiag_validate.argtypes = [pi32, pi32, pi32, i32, i32, i32, i32, i32]
     lib.blockdiag_validate.restype = ctypes.c_int
+    prange = ctypes.POINTER(KvRange)
+    lib.blockdiag_kv_plan.argtypes = [pi32, pi32, i32, i32, i32, i32, i32, pi32, pi32, i32, prange, pi32, prange,
+                                      pi32, pi32, pi32]
+    lib.blockdiag_kv_plan.restype = ctypes.c_int
     lib.blockdiag_meta_ints.argtypes = [i32, i32, i32]
     lib.blockdiag_meta_ints.restype = sz
     pdesc = ctypes.POINTER(MetaDesc)
-    lib.blockdiag_meta_build.argtypes = [p, i32, i32, i32, i32, i32, p, sz, pdesc, p]
+    lib.blockdiag_meta_build.argtypes = [p, pi32, i32, i32, i32, i32, i32, p, sz, pdesc, p]
     lib.blockdiag_meta_build.restype = ctypes.c_int
     lib.blockdiag_meta_build_host.argtypes = [pi32, i32, i32, i32, i32, i32, p, sz, pdesc, p]
     lib.blockdiag_meta_build_host.restype = ctypes.c_int
@@ -100,14 +112,14 @@ def load_library():
     lib.blockdiag_meta_inline_max_seg.restype = i32
     lib.blockdiag_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, i32, i32, i32]
     lib.blockdiag_workspace_bytes.restype = sz
-    lib.blockdiag_attn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
-                                       p, p, p, pdesc, p, p, p, sz, p]
+    lib.blockdiag_attn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float, p, p, p, pdesc, p, p, p, sz, p]
     lib.blockdiag_attn_fwd.restype = ctypes.c_int
-    lib.blockdiag_attn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
-                                       p, p, p, p, p, p, pdesc, p, p, p, p, sz, p]
+    lib.blockdiag_attn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float, p, p, p, p, p, p, pdesc, p, p, p, p, sz, p]
     lib.blockdiag_attn_bwd.restype = ctypes.c_int
-    lib.blockdiag_attn_bwd_noalloc.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, ctypes.c_float,
-                                               p, p, p, p, p, p, pdesc, p, p, p, p]
+    lib.blockdiag_attn_bwd_noalloc.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                               ctypes.c_float, p, p, p, p, p, p, pdesc, p, p, p, p]
     lib.blockdiag_attn_bwd_noalloc.restype = ctypes.c_int
     lib.blockdiag_noalloc_scratch_bytes.argtypes = []
     lib.blockdiag_noalloc_scratch_bytes.restype = sz
@@ -179,7 +191,7 @@ class SegTable:
                 return dataclasses.replace(self, table=None, meta=meta, desc=desc, _pinned=None)
             pinned = torch.from_numpy(flat).pin_memory()
             table = pinned.to(meta.device, non_blocking=True)  # no host sync; pinned copy kept alive below
-            _check(lib.blockdiag_meta_build(table.data_ptr(), self.n_seg, self.batch, self.seq_len,
+            _check(lib.blockdiag_meta_build(table.data_ptr(), _ptr(flat), self.n_seg, self.batch, self.seq_len,
                                             self.row_offset, self.q_len, meta.data_ptr(), meta.numel(),
                                             ctypes.byref(desc), stream))
         return dataclasses.replace(self, table=table, meta=meta, desc=desc, _pinned=pinned)
@@ -288,14 +300,18 @@ def _dtype_code(t):
     raise BlockdiagError(5, f"dtype {t.dtype} not supported (float32 or bfloat16)")
 
 
-def _shapes(q, k, v, seg):
+def _shapes(q, k, v, seg, kv_begin=0):
+    """Checks the tensors against the segment table; k, v hold keys
+    [kv_begin, kv_begin + k.shape[1]) of every row (the whole row when
+    kv_begin = 0 and k.shape[1] = S)."""
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise BlockdiagError(1, "q must be [B, q_len, H_q, d] and k, v [B, S, H_kv, d]")
+        raise BlockdiagError(1, "q must be [B, q_len, H_q, d] and k, v [B, kv_len, H_kv, d]")
     B, L, Hq, d = q.shape
-    Bk, S, Hkv, dk = k.shape
-    if Bk != B or dk != d or B != seg.batch or S != seg.seq_len or L != seg.q_len:
-        raise BlockdiagError(1, f"shapes q{tuple(q.shape)} k{tuple(k.shape)} do not match the "
-                                f"segment table (B={seg.batch}, S={seg.seq_len}, q_len={seg.q_len})")
+    Bk, W, Hkv, dk = k.shape
+    S = seg.seq_len
+    if Bk != B or dk != d or B != seg.batch or L != seg.q_len or not 0 <= kv_begin <= kv_begin + W <= S:
+        raise BlockdiagError(1, f"shapes q{tuple(q.shape)} k{tuple(k.shape)} (K/V from key {kv_begin}) do not "
+                                f"match the segment table (B={seg.batch}, S={seg.seq_len}, q_len={seg.q_len})")
     if q.device.type != "cuda":
         raise BlockdiagError(1, "q, k, v must be contiguous device tensors of one dtype")
     for t in (q, k, v):
@@ -303,7 +319,7 @@ def _shapes(q, k, v, seg):
             raise BlockdiagError(1, "q, k, v must be contiguous device tensors of one dtype on one device")
     if seg.meta is None or seg.desc is None or seg.meta.device != q.device:
         raise BlockdiagError(1, "segment table has no device metadata on the tensors' device")
-    return B, L, Hq, d, S, Hkv
+    return B, L, Hq, d, S, Hkv, W
 
 
 def mark_main_kernel(start_event, stop_event):
@@ -313,11 +329,13 @@ def mark_main_kernel(start_event, stop_event):
     _check(load_library().blockdiag_mark_main_kernel(start_event, stop_event))
 
 
-def attn_fwd(q, k, v, seg, scale=None):
-    """O and LSE of the chunk (``blockdiag_attn_fwd``)."""
+def attn_fwd(q, k, v, seg, scale=None, kv_begin=0):
+    """O and LSE of the chunk (``blockdiag_attn_fwd``).  ``k``, ``v`` hold
+    keys [kv_begin, kv_begin + k.shape[1]) of every row: the whole row
+    (default) or a window with every key the chunk attends (``kv_plan``)."""
     import torch
     lib = load_library()
-    B, L, Hq, d, S, Hkv = _shapes(q, k, v, seg)
+    B, L, Hq, d, S, Hkv, W = _shapes(q, k, v, seg, kv_begin)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _dtype_code(q)
     o = torch.empty_like(q)
@@ -326,17 +344,18 @@ def attn_fwd(q, k, v, seg, scale=None):
     ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):  # the library launches on the current device
-        _check(lib.blockdiag_attn_fwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(),
+        _check(lib.blockdiag_attn_fwd(dt, B, S, seg.row_offset, L, kv_begin, W, Hq, Hkv, d, scale, q.data_ptr(),
                                       k.data_ptr(), v.data_ptr(), ctypes.byref(seg.desc), o.data_ptr(),
                                       lse.data_ptr(), ws.data_ptr(), ws_bytes, stream))
     return o, lse
 
 
-def attn_bwd(q, k, v, o, lse, do, seg, scale=None):
-    """dQ, dK, dV of the loss sum(dO * O) (``blockdiag_attn_bwd``)."""
+def attn_bwd(q, k, v, o, lse, do, seg, scale=None, kv_begin=0):
+    """dQ, dK, dV of the loss sum(dO * O) (``blockdiag_attn_bwd``); dK, dV
+    cover the same keys as ``k``, ``v``."""
     import torch
     lib = load_library()
-    B, L, Hq, d, S, Hkv = _shapes(q, k, v, seg)
+    B, L, Hq, d, S, Hkv, W = _shapes(q, k, v, seg, kv_begin)
     for t in (o, do):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise BlockdiagError(1, "o and do must match q (shape, dtype, device, contiguous)")
@@ -352,11 +371,56 @@ def attn_bwd(q, k, v, o, lse, do, seg, scale=None):
     ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):  # the library launches on the current device
-        _check(lib.blockdiag_attn_bwd(dt, B, S, seg.row_offset, L, Hq, Hkv, d, scale, q.data_ptr(),
+        _check(lib.blockdiag_attn_bwd(dt, B, S, seg.row_offset, L, kv_begin, W, Hq, Hkv, d, scale, q.data_ptr(),
                                       k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                       do.data_ptr(), ctypes.byref(seg.desc), dq.data_ptr(), dk.data_ptr(),
                                       dv.data_ptr(), ws.data_ptr(), ws_bytes, stream))
     return dq, dk, dv
+
+
+@dataclasses.dataclass
+class KvPlan:
+    """Needed-only K/V exchange plan of one context-parallel rank
+    (``blockdiag_kv_plan``): the K/V window [kv_begin, kv_end) the rank's
+    attention calls take, the ranges it receives and sends as lists of
+    (row, peer, begin, end), and the rank's and the step's exchange mode
+    (0 none, 1 left-neighbour halo, 2 all-to-all-v)."""
+    cp: int
+    rank: int
+    kv_begin: int
+    kv_end: int
+    recv: list
+    send: list
+    rank_mode: int
+    step_mode: int
+
+
+def kv_plan(doc_lens_rows, seq_len, cp, rank, align=64):
+    """Needed-only K/V plan of rank ``rank`` of ``cp`` contiguous chunks
+    (``blockdiag_kv_plan``)."""
+    lib = load_library()
+    rows = [np.asarray(r, dtype=np.int64).ravel() for r in doc_lens_rows]
+    flat = np.concatenate(rows).astype(np.int32) if rows and sum(len(r) for r in rows) else np.zeros(1, np.int32)
+    per = np.array([len(r) for r in rows] or [0], dtype=np.int32)
+    cap = 16
+    while True:
+        recv = (KvRange * cap)()
+        send = (KvRange * cap)()
+        vals = [ctypes.c_int32(0) for _ in range(6)]
+        code = lib.blockdiag_kv_plan(_ptr(flat), _ptr(per), len(rows), int(seq_len), int(cp), int(rank), int(align),
+                                     ctypes.byref(vals[0]), ctypes.byref(vals[1]), cap, recv, ctypes.byref(vals[2]),
+                                     send, ctypes.byref(vals[3]), ctypes.byref(vals[4]), ctypes.byref(vals[5]))
+        if code == 3:
+            cap = max(vals[2].value, vals[3].value)
+            continue
+        _check(code)
+        break
+    kb, ke, nr, ns, rm, sm = (x.value for x in vals)
+
+    def rng(arr, n):
+        return [(arr[i].row, arr[i].peer, arr[i].begin, arr[i].end) for i in range(n)]
+
+    return KvPlan(int(cp), int(rank), kb, ke, rng(recv, nr), rng(send, ns), rm, sm)
 
 
 def _autograd_fn():
@@ -364,18 +428,19 @@ def _autograd_fn():
 
     class _BlockdiagAttention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, seg, scale):
-            o, lse = attn_fwd(q, k, v, seg, scale)
+        def forward(ctx, q, k, v, seg, scale, kv_begin):
+            o, lse = attn_fwd(q, k, v, seg, scale, kv_begin)
             ctx.save_for_backward(q, k, v, o, lse)
             ctx.seg = seg
             ctx.scale = scale
+            ctx.kv_begin = kv_begin
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.seg, ctx.scale)
-            return dq, dk, dv, None, None
+            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.seg, ctx.scale, ctx.kv_begin)
+            return dq, dk, dv, None, None, None
 
     return _BlockdiagAttention
 
@@ -383,10 +448,11 @@ def _autograd_fn():
 _FN = None
 
 
-def attention(q, k, v, seg, scale=None):
+def attention(q, k, v, seg, scale=None, kv_begin=0):
     """Drop-in attention over a packed chunk with autograd (Design overview,
-    runtime.py: a drop-in SDPA; packed.py: row_offset = 0 for one GPU)."""
+    runtime.py: a drop-in SDPA; packed.py: row_offset = 0 for one GPU);
+    ``kv_begin`` as for ``attn_fwd``."""
     global _FN
     if _FN is None:
         _FN = _autograd_fn()
-    return _FN.apply(q, k, v, seg, scale)
+    return _FN.apply(q, k, v, seg, scale, kv_begin)

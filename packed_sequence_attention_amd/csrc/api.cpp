@@ -16,9 +16,12 @@ using bd::fail;
 namespace {
 
 constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+// Start alignment of a K/V window: the largest key tile of any kernel.
+constexpr int32_t kKvAlign = 64;
 
 bd_status check_common(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
-                       int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim, float scale) {
+                       int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q, int32_t h_kv,
+                       int32_t head_dim, float scale) {
   if (dtype != BD_F32 && dtype != BD_BF16) return fail(BD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
   if (batch < 0 || seq_len < 0 || row_offset < 0 || q_len < 0)
     return fail(BD_ERR_INVALID_ARG, "negative size");
@@ -29,16 +32,26 @@ bd_status check_common(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t r
   if (head_dim <= 0 || head_dim > 256 || head_dim % 8 != 0)
     return fail(BD_ERR_UNSUPPORTED, "head_dim %d: supported are multiples of 8 up to 256", head_dim);
   if (!isfinite(scale)) return fail(BD_ERR_INVALID_ARG, "scale must be finite");
+  // K/V window [kv_begin, kv_begin + kv_len): tile-aligned start (so no key
+  // tile starts before the buffer), inside the row, reaching the chunk's end.
+  if (kv_begin < 0 || kv_len < 0 || static_cast<int64_t>(kv_begin) + kv_len > seq_len)
+    return fail(BD_ERR_INVALID_ARG, "K/V window [%d, %d + %d) outside the row of %d keys", kv_begin, kv_begin,
+                kv_len, seq_len);
+  if (kv_begin % kKvAlign != 0)
+    return fail(BD_ERR_INVALID_ARG, "K/V window start %d is not a multiple of %d", kv_begin, kKvAlign);
+  if (kv_begin > row_offset || static_cast<int64_t>(kv_begin) + kv_len < static_cast<int64_t>(row_offset) + q_len)
+    return fail(BD_ERR_INVALID_ARG, "K/V window [%d, %d) does not cover the chunk [%d, %d)", kv_begin,
+                kv_begin + kv_len, row_offset, row_offset + q_len);
   const int64_t nq = static_cast<int64_t>(batch) * q_len * h_q * head_dim;
-  const int64_t nk = static_cast<int64_t>(batch) * seq_len * h_kv * head_dim;
+  const int64_t nk = static_cast<int64_t>(batch) * kv_len * h_kv * head_dim;
   if (nq > kMaxElems || nk > kMaxElems || static_cast<int64_t>(batch) * seq_len > kMaxElems)
     return fail(BD_ERR_INVALID_ARG, "tensor too large for 32-bit element counts");
   return BD_OK;
 }
 
-bool use_mfma_fwd(bd_dtype dtype, int32_t seq_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
+bool use_mfma_fwd(bd_dtype dtype, int32_t kv_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
   return bd::mfma_fwd_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f &&
-         bd::fwd_mfma_fits(seq_len, h_kv, head_dim);
+         bd::fwd_mfma_fits(kv_len, h_kv, head_dim);
 }
 
 bool use_mfma_bwd(bd_dtype dtype, int32_t q_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
@@ -46,16 +59,17 @@ bool use_mfma_bwd(bd_dtype dtype, int32_t q_len, int32_t head_dim, int32_t h_q, 
          bd::bwd_mfma_fits(q_len, h_q, head_dim);
 }
 
-bool use_mfma_bwd_full(bd_dtype dtype, int32_t seq_len, int32_t q_len, int32_t head_dim, int32_t h_q,
+bool use_mfma_bwd_full(bd_dtype dtype, int32_t kv_len, int32_t q_len, int32_t head_dim, int32_t h_q,
                        int32_t h_kv, float scale) {
-  return use_mfma_bwd(dtype, q_len, head_dim, h_q, h_kv, scale) && bd::bwd_dq_fits(seq_len, h_kv, head_dim);
+  return use_mfma_bwd(dtype, q_len, head_dim, h_q, h_kv, scale) && bd::bwd_dq_fits(kv_len, h_kv, head_dim);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // O(1) host check that a metadata descriptor was built for this call's sizes
 // (the kernels index the buffer with the call's batch, seq_len and q_len).
-bd_status check_meta(const bd_meta* m, int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len) {
+bd_status check_meta(const bd_meta* m, int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len,
+                     int32_t kv_begin, int32_t kv_len) {
   if (m == nullptr) return fail(BD_ERR_INVALID_ARG, "null metadata descriptor");
   if (m->magic != BD_META_MAGIC) return fail(BD_ERR_INVALID_ARG, "metadata descriptor was not built");
   if (m->batch != batch || m->seq_len != seq_len || m->row_offset != row_offset || m->q_len != q_len)
@@ -67,6 +81,9 @@ bd_status check_meta(const bd_meta* m, int32_t batch, int32_t seq_len, int32_t r
     return fail(BD_ERR_INVALID_ARG, "metadata holds %llu ints, %zu needed",
                 static_cast<unsigned long long>(m->n_ints), need);
   if (need > 0 && m->data == nullptr) return fail(BD_ERR_INVALID_ARG, "null metadata buffer");
+  if (kv_begin > m->kv_lo || static_cast<int64_t>(kv_begin) + kv_len < m->kv_hi)
+    return fail(BD_ERR_INVALID_ARG, "K/V window [%d, %d) misses keys the chunk attends: [%d, %d)", kv_begin,
+                kv_begin + kv_len, m->kv_lo, m->kv_hi);
   return BD_OK;
 }
 
@@ -91,8 +108,40 @@ bd_status check_meta_build(const int32_t* table, int32_t n_seg, int32_t batch, i
   return BD_OK;
 }
 
+// Keys the chunk attends over all batch rows, [*lo, *hi), from a host copy
+// of the segment table: the union of the non-padding segments' key ranges
+// (row coordinates); [row_offset, row_offset) when no row attends a key.
+// Without the table: [0, row_offset + q_len), which admits only windows that
+// start at key 0.
+void table_window(const int32_t* h_table, int32_t n_seg, int32_t seq_len, int32_t row_offset, int32_t q_len,
+                  int32_t* lo, int32_t* hi) {
+  if (h_table == nullptr) {
+    *lo = 0;
+    *hi = row_offset + q_len;
+    return;
+  }
+  const int32_t* cu_q = h_table;
+  const int32_t* cu_k = h_table + n_seg + 1;
+  const int32_t* kb = h_table + 2 * (n_seg + 1);
+  int64_t wlo = row_offset, whi = row_offset;
+  bool any = false;
+  for (int32_t s = 0; s < n_seg; ++s) {
+    const int64_t kn = static_cast<int64_t>(cu_k[s + 1]) - cu_k[s];
+    if (kn <= 0 || q_len <= 0 || seq_len <= 0) continue;
+    const int64_t b = cu_q[s] / q_len;
+    const int64_t a = static_cast<int64_t>(kb[s]) - b * seq_len;
+    wlo = any ? (a < wlo ? a : wlo) : a;
+    whi = any ? (a + kn > whi ? a + kn : whi) : a + kn;
+    any = true;
+  }
+  *lo = static_cast<int32_t>(wlo);
+  *hi = static_cast<int32_t>(whi);
+}
+
 void fill_desc(bd_meta* desc, int32_t n_seg, int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len,
-               const int32_t* d_meta) {
+               const int32_t* d_meta, const int32_t* h_table) {
+  table_window(h_table, n_seg, seq_len, row_offset, q_len, &desc->kv_lo, &desc->kv_hi);
+  desc->reserved = 0;
   desc->batch = batch;
   desc->seq_len = seq_len;
   desc->row_offset = row_offset;
@@ -131,8 +180,8 @@ extern "C" size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_
          bd::meta_order_ints(batch, seq_len, q_len);
 }
 
-extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, int32_t n_seg, int32_t batch,
-                                          int32_t seq_len, int32_t row_offset, int32_t q_len,
+extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, const int32_t* h_table, int32_t n_seg,
+                                          int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len,
                                           int32_t* d_meta, size_t meta_capacity, bd_meta* desc,
                                           void* stream) {
   bd::clear_error();
@@ -143,7 +192,7 @@ extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, int32_t n_seg,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
   }
-  fill_desc(desc, n_seg, batch, seq_len, row_offset, q_len, d_meta);
+  fill_desc(desc, n_seg, batch, seq_len, row_offset, q_len, d_meta, h_table);
   return BD_OK;
 }
 
@@ -164,7 +213,7 @@ extern "C" bd_status blockdiag_meta_build_host(const int32_t* h_table, int32_t n
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BD_ERR_HIP, "meta_build launch: %s", hipGetErrorString(e));
   }
-  fill_desc(desc, n_seg, batch, seq_len, row_offset, q_len, d_meta);
+  fill_desc(desc, n_seg, batch, seq_len, row_offset, q_len, d_meta, h_table);
   return BD_OK;
 }
 
@@ -177,38 +226,40 @@ extern "C" size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t 
 }
 
 extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
-                                        int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                                        int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
+                                        int32_t h_kv, int32_t head_dim,
                                         float scale, const void* q, const void* k, const void* v,
                                         const bd_meta* meta, void* o, float* lse, void* workspace,
                                         size_t workspace_bytes, void* stream) {
   bd::clear_error();
   (void)workspace;
-  bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale);
+  bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim, scale);
   if (st != BD_OK) return st;
   if (batch == 0 || q_len == 0) return BD_OK;
   if (!q || !k || !v || !o || !lse) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
-  st = check_meta(meta, batch, seq_len, row_offset, q_len);
+  st = check_meta(meta, batch, seq_len, row_offset, q_len, kv_begin, kv_len);
   if (st != BD_OK) return st;
   const size_t need = blockdiag_workspace_bytes(0, dtype, batch, seq_len, q_len, h_q, h_kv, head_dim);
   if (workspace_bytes < need) return fail(BD_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-  bd::FwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
-                q, k, v, meta->data, o, lse, nullptr, nullptr};
+  bd::FwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim,
+                scale, q, k, v, meta->data, o, lse, nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = use_mfma_fwd(dtype, seq_len, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
+  hipError_t e = use_mfma_fwd(dtype, kv_len, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
                                                                           : bd::launch_fwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return BD_OK;
 }
 
 extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
-                                        int32_t q_len, int32_t h_q, int32_t h_kv, int32_t head_dim,
+                                        int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
+                                        int32_t h_kv, int32_t head_dim,
                                         float scale, const void* q, const void* k, const void* v,
                                         const void* o, const float* lse, const void* d_o,
                                         const bd_meta* meta, void* dq, void* dk, void* dv,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   bd::clear_error();
-  bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale);
+  bd_status st = check_common(dtype, batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim, scale);
   if (st != BD_OK) return st;
   if (batch == 0) return BD_OK;
   if (!k || !v || !dk || !dv) return fail(BD_ERR_INVALID_ARG, "null tensor pointer");
@@ -219,16 +270,16 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (q_len == 0) {
     // No local rows: the chunk's partial dK/dV are zero.
-    const int64_t words = static_cast<int64_t>(batch) * seq_len * h_kv * head_dim * (dtype == BD_F32 ? 2 : 1);
+    const int64_t words = static_cast<int64_t>(batch) * kv_len * h_kv * head_dim * (dtype == BD_F32 ? 2 : 1);
     hipError_t e = bd::launch_zero_u16(dk, words, s);
     if (e == hipSuccess) e = bd::launch_zero_u16(dv, words, s);
     if (e != hipSuccess) return fail(BD_ERR_HIP, "zero-fill: %s", hipGetErrorString(e));
     return BD_OK;
   }
-  st = check_meta(meta, batch, seq_len, row_offset, q_len);
+  st = check_meta(meta, batch, seq_len, row_offset, q_len, kv_begin, kv_len);
   if (st != BD_OK) return st;
-  const bool mf = use_mfma_bwd_full(dtype, seq_len, q_len, head_dim, h_q, h_kv, scale);
-  bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, scale,
+  const bool mf = use_mfma_bwd_full(dtype, kv_len, q_len, head_dim, h_q, h_kv, scale);
+  bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim, scale,
                 q, k, v, o, lse, d_o, meta->data, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);

@@ -120,9 +120,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   const int kt = slot % n_kt;
   if (bg >= n_bg) return;  // whole workgroup: no barrier has been reached
   const int b = bg / s.h_kv, g = bg % s.h_kv;
-  const int key = kt * kKB + kgrp * kKW + n;  // this lane's key (columns of S)
-  const bool key_ok = key < s.seq_len;
-  const int64_t kv_row = (static_cast<int64_t>(b) * s.seq_len + key) * s.h_kv + g;
+  const int key0 = s.kv_begin + kt * kKB;  // the workgroup's first key (row position)
+  const int key = key0 + kgrp * kKW + n;  // this lane's key (columns of S)
+  // key is a position in the row; K/V/dK/dV hold keys [kv_begin, kv_begin +
+  // kv_len) of every row (key tiles are counted from kv_begin).
+  const bool key_ok = key < s.kv_begin + s.kv_len;
+  const int64_t kv_row = (static_cast<int64_t>(b) * s.kv_len + (key - s.kv_begin)) * s.h_kv + g;
 
   // Local rows attending this lane's key: [a0, a1) when a1 > a0 (loaded
   // here, used after the other prologue loads have been issued).
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // attends them.  Its loads go out with the K / V / metadata loads (one
   // memory round trip for the prologue instead of two); the metadata only
   // confirms the tile below.
-  const int qt0e = max(kt * kKB - s.row_offset, 0) / kQB;
+  const int qt0e = max(key0 - s.row_offset, 0) / kQB;
   const bool early = qt0e * kQB < s.q_len;
   if (early) issue_tile(g * s.group + hsub, qt0e * kQB, 0);
 
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // Loads without branches (keys past the row read the row's last key and
   // are zeroed where the values are used), so that no load waits for the
   // ones issued before it.
-  const int64_t kv_row_c = key_ok ? kv_row : (static_cast<int64_t>(b) * s.seq_len + s.seq_len - 1) * s.h_kv + g;
+  const int64_t kv_row_c = key_ok ? kv_row : (static_cast<int64_t>(b) * s.kv_len + s.kv_len - 1) * s.h_kv + g;
   bf16x8 kf[KK];
   char* sV = vt + kgrp * kKW * L::QP;
 #pragma unroll
@@ -517,8 +520,9 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   AttnShape s;
   s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
   s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
+  s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
-  const int n_kt = (a.seq_len + kKB - 1) / kKB;
+  const int n_kt = (a.kv_len + kKB - 1) / kKB;
   const int n_bg = a.batch * a.h_kv;
   const int64_t grid = 8 * static_cast<int64_t>((n_bg + 7) / 8) * n_kt;
   if (n_kt == 0) return hipSuccess;

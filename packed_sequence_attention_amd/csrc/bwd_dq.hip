@@ -142,9 +142,12 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
       ov[kk] = *reinterpret_cast<const bf16x8*>(o + row + kk * 16);
     }
   }
-  const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
+  // The K/V buffer holds keys [kv_begin, kv_begin + kv_len) of every row;
+  // kv0 is its first key of (b, g).  Visited tiles start at or after
+  // kv_begin (a multiple of 64), so a tile's offset from there is >= 0.
+  const int64_t kv0 = (static_cast<int64_t>(b) * s.kv_len * s.h_kv + g) * D;
   const int kv_stride = s.h_kv * D;
-  const int kv_bytes = (s.seq_len * kv_stride - g * D) * 2;
+  const int kv_bytes = (s.kv_len * kv_stride - g * D) * 2;
   // Direct load c (of 2 NCH: K and V chunks alternately) of key tile kt into
   // stage buf.  The loads of the next tile are spread over the first S/dP
   // block (one per step): issued together, a workgroup's loads queue up at
@@ -167,9 +170,9 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
     char* sK = buf == 0 ? stage0 : stage1;
     char* dst = (c & 1) ? sK + kBN * RP : sK;
     const int i = c >> 1;
-    const int tile_off = kt * kBN * kv_stride;  // elements
+    const int tile_off = (kt * kBN - s.kv_begin) * kv_stride;  // elements from key kv_begin
     const int vo = dma_off[i];
-    const int nbytes = live ? kv_bytes - tile_off * 2 : 0;
+    const int nbytes = live ? max(kv_bytes - tile_off * 2, 0) : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(((c & 1) ? v : k) + kv0 + tile_off), 0, nbytes, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16,
@@ -235,7 +238,9 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
 
   if (kmax > kmin) {
-    const int kt0 = kmin / kBN;  // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked
+    // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked; none before the
+    // K/V buffer's first key (clamped as in the forward).
+    const int kt0 = max(kmin, s.kv_begin) / kBN;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Unrolled by two so that the stage is a compile-time constant.
@@ -355,6 +360,7 @@ hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
   AttnShape s;
   s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
   s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
+  s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int n_qt = (a.q_len + kBM - 1) / kBM;
   const int n_hg = a.h_q / 4;
@@ -369,10 +375,10 @@ hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim) {
+bool bwd_dq_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim) {
   // a (batch row, K/V head)'s keys, including the last tile's keys past the
-  // row, must be addressable with 31-bit buffer offsets
-  return (seq_len + kBNmax) * h_kv * head_dim * 2 < (int64_t{1} << 31);
+  // window, must be addressable with 31-bit buffer offsets
+  return (kv_len + kBNmax) * h_kv * head_dim * 2 < (int64_t{1} << 31);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {

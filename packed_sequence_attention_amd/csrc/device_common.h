@@ -89,6 +89,10 @@ __device__ __forceinline__ int wave_max_i(int x) {
 struct AttnShape {
   int batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim, group;
   float scale;
+  // K/V (and dK/dV) hold keys [kv_begin, kv_begin + kv_len) of every row,
+  // kv_begin a multiple of 64 (the whole row: 0 and seq_len).  Positions in
+  // the metadata and the masks stay those of the row.
+  int kv_begin, kv_len;
 };
 
 // Query-tile order: the metadata build also writes, for the 32-row query

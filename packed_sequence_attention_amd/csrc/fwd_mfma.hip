@@ -157,9 +157,12 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
   // resource) and writes zeros into the free stage: it is issued without a
   // branch, which would split the S block and stop the scheduler from
   // overlapping its LDS reads with the products.
-  const int64_t kv0 = (static_cast<int64_t>(b) * s.seq_len * s.h_kv + g) * D;  // key 0 of (b, g)
+  // The K/V buffer holds keys [kv_begin, kv_begin + kv_len) of every row;
+  // kv0 is its first key of (b, g).  Visited tiles start at or after
+  // kv_begin (a multiple of 64), so a tile's offset from there is >= 0.
+  const int64_t kv0 = (static_cast<int64_t>(b) * s.kv_len * s.h_kv + g) * D;
   const int kv_stride = s.h_kv * D;
-  const int kv_bytes = (s.seq_len * kv_stride - g * D) * 2;
+  const int kv_bytes = (s.kv_len * kv_stride - g * D) * 2;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Per-lane part of the offsets of load i (K and V tiles share it); the
   // tile's row offset goes into the resource base.
@@ -174,9 +177,9 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
     char* sK = buf == 0 ? stage0 : stage1;
     char* dst = (c & 1) ? sK + kBN * RP : sK;
     const int i = c >> 1;
-    const int tile_off = kt * kBN * kv_stride;  // elements
+    const int tile_off = (kt * kBN - s.kv_begin) * kv_stride;  // elements from key kv_begin
     const int vo = dma_off[i];
-    const int nbytes = live ? kv_bytes - tile_off * 2 : 0;
+    const int nbytes = live ? max(kv_bytes - tile_off * 2, 0) : 0;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(((c & 1) ? v : k) + kv0 + tile_off), 0, nbytes, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (i * 256 + wave_u * 64) * 16), 16,
@@ -229,7 +232,10 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
   }
 
   if (kmax > kmin) {
-    const int kt0 = kmin / kBN;  // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked
+    // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked.  No tile before
+    // the K/V buffer's first key is visited (the host checks that the rows'
+    // keys lie in the buffer; the clamp keeps a mismatched table in bounds).
+    const int kt0 = max(kmin, s.kv_begin) / kBN;
     if (!valid) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
@@ -361,6 +367,7 @@ hipError_t fwd_mfma_t(const FwdArgs& a, hipStream_t st) {
   AttnShape s;
   s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
   s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
+  s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int n_qt = (a.q_len + kBM - 1) / kBM;
   const int n_hg = a.h_q / 4;
@@ -387,10 +394,10 @@ bool mfma_fwd_supported(int dtype, int head_dim, int h_q, int h_kv) {
   return mfma_supported(dtype, head_dim, h_q, h_kv) || (head_dim == 256 && mfma_supported(dtype, 128, h_q, h_kv));
 }
 
-bool fwd_mfma_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim) {
+bool fwd_mfma_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim) {
   // a (batch row, K/V head)'s keys, including the last tile's keys past the
-  // row, must be addressable with 31-bit buffer offsets
-  return (seq_len + kBN) * h_kv * head_dim * 2 < (int64_t{1} << 31);
+  // window, must be addressable with 31-bit buffer offsets
+  return (kv_len + kBN) * h_kv * head_dim * 2 < (int64_t{1} << 31);
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {

@@ -81,8 +81,10 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(AttnShape s, const T* 
   const T* qrow = q + (bt * s.h_q + h) * D;
   for (int d = lane; d < D; d += 64) sq[wave][d] = Elem<T>::load(qrow + d);
   wave_sync();
-  const int lo = m.row_lo[bt], hi = m.row_hi[bt];
-  const int64_t kv_base = static_cast<int64_t>(b) * s.seq_len;
+  // keys of the K/V window only (the host checks that it holds every key
+  // the rows attend; the clamp keeps a mismatched table in bounds)
+  const int lo = max(m.row_lo[bt], s.kv_begin), hi = min(m.row_hi[bt], s.kv_begin + s.kv_len);
+  const int64_t kv_base = static_cast<int64_t>(b) * s.kv_len - s.kv_begin;  // row position j -> window row
   float mrun = -INFINITY, lrun = 0.f, acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = 0.f;
@@ -151,11 +153,11 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
     sdo[wave][d] = Elem<T>::load(d_o + row + d);
   }
   wave_sync();
-  const int lo = m.row_lo[bt], hi = m.row_hi[bt];
+  const int lo = max(m.row_lo[bt], s.kv_begin), hi = min(m.row_hi[bt], s.kv_begin + s.kv_len);
   const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
   const float lse_t = hi > lo ? lse[st] : 0.f;
   const float delta_t = rowstat[2 * st + 1];
-  const int64_t kv_base = static_cast<int64_t>(b) * s.seq_len;
+  const int64_t kv_base = static_cast<int64_t>(b) * s.kv_len - s.kv_begin;  // row position j -> window row
   float acc[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) acc[r] = 0.f;
@@ -206,13 +208,14 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
   __shared__ float sds[kWaves][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  const int64_t total = static_cast<int64_t>(s.batch) * s.seq_len * s.h_kv;
+  const int64_t total = static_cast<int64_t>(s.batch) * s.kv_len * s.h_kv;  // the window's keys
   if (w >= total) return;
   const int D = s.head_dim;
   const int g = static_cast<int>(w % s.h_kv);
-  const int64_t bj = w / s.h_kv;
-  const int b = static_cast<int>(bj / s.seq_len);
-  const int64_t krow = (bj * s.h_kv + g) * D;
+  const int64_t bw = w / s.h_kv;  // b * kv_len + window row
+  const int b = static_cast<int>(bw / s.kv_len);
+  const int64_t bj = static_cast<int64_t>(b) * s.seq_len + s.kv_begin + bw % s.kv_len;  // metadata index
+  const int64_t krow = (bw * s.h_kv + g) * D;
   for (int d = lane; d < D; d += 64) {
     sk[wave][d] = Elem<T>::load(k + krow + d);
     sv[wave][d] = Elem<T>::load(v + krow + d);
@@ -304,11 +307,12 @@ int lanes_per_row(int head_dim) {
   return l;
 }
 
-AttnShape make_shape(int batch, int seq_len, int row_offset, int q_len, int h_q, int h_kv,
-                     int head_dim, float scale) {
+AttnShape make_shape(int batch, int seq_len, int row_offset, int q_len, int kv_begin, int kv_len, int h_q,
+                     int h_kv, int head_dim, float scale) {
   AttnShape s;
   s.batch = batch; s.seq_len = seq_len; s.row_offset = row_offset; s.q_len = q_len;
   s.h_q = h_q; s.h_kv = h_kv; s.head_dim = head_dim; s.group = h_q / h_kv; s.scale = scale;
+  s.kv_begin = kv_begin; s.kv_len = kv_len;
   return s;
 }
 
@@ -316,7 +320,8 @@ unsigned blocks_for(int64_t waves) { return static_cast<unsigned>((waves + kWave
 
 template <typename T, int NR>
 hipError_t fwd_generic_t(const FwdArgs& a, hipStream_t st) {
-  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
+  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.kv_begin, a.kv_len, a.h_q, a.h_kv, a.head_dim,
+                           a.scale);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int64_t waves = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
   hipError_t e = mark(a.mark_start, st);
@@ -331,7 +336,8 @@ hipError_t fwd_generic_t(const FwdArgs& a, hipStream_t st) {
 
 template <typename T, int NR>
 hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
-  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.h_q, a.h_kv, a.head_dim, a.scale);
+  AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.kv_begin, a.kv_len, a.h_q, a.h_kv, a.head_dim,
+                           a.scale);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
   const int lpr = lanes_per_row(a.head_dim);
@@ -344,7 +350,7 @@ hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
       static_cast<const T*>(a.d_o), a.lse, a.rowstat, m, static_cast<T*>(a.dq));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t keys = static_cast<int64_t>(a.batch) * a.seq_len * a.h_kv;
+  const int64_t keys = static_cast<int64_t>(a.batch) * a.kv_len * a.h_kv;
   e = mark(a.mark_start, st);
   if (e != hipSuccess) return e;
   dkv_generic_kernel<T, NR><<<blocks_for(keys), 256, 0, st>>>(

@@ -11,7 +11,9 @@ namespace bd {
 
 struct FwdArgs {
   int dtype;  // 0 = f32, 1 = bf16
-  int batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim;
+  int batch, seq_len, row_offset, q_len;
+  int kv_begin, kv_len;  // k, v hold keys [kv_begin, kv_begin + kv_len) of every row
+  int h_q, h_kv, head_dim;
   float scale;
   const void* q;
   const void* k;
@@ -25,7 +27,9 @@ struct FwdArgs {
 
 struct BwdArgs {
   int dtype;
-  int batch, seq_len, row_offset, q_len, h_q, h_kv, head_dim;
+  int batch, seq_len, row_offset, q_len;
+  int kv_begin, kv_len;  // k, v, dk, dv hold keys [kv_begin, kv_begin + kv_len) of every row
+  int h_q, h_kv, head_dim;
   float scale;
   const void* q;
   const void* k;
@@ -64,15 +68,15 @@ bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv);
 // the same with head_dim 256 as well (forward, dQ and the head_dim-256 dK/dV
 // kernel).
 bool mfma_fwd_supported(int dtype, int head_dim, int h_q, int h_kv);
-// The matrix-core forward addresses a (batch row, K/V head)'s keys with
-// 31-bit buffer offsets; larger rows take the generic kernel.
-bool fwd_mfma_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim);
+// The matrix-core forward addresses a (batch row, K/V head)'s keys (the K/V
+// window) with 31-bit buffer offsets; larger rows take the generic kernel.
+bool fwd_mfma_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t stream);
 // The matrix-core backward addresses one (batch row, head)'s Q / dO rows and
 // one (batch row, K/V head)'s keys with 32-bit buffer offsets.
 bool bwd_mfma_fits(int64_t q_len, int64_t h_q, int64_t head_dim);
-bool bwd_dq_fits(int64_t seq_len, int64_t h_kv, int64_t head_dim);
+bool bwd_dq_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim);
 // dQ of the matrix-core backward (query-stationary); also writes rowstat.
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 // dK / dV of the matrix-core backward at head_dim 256 (bwd_dkdv256.hip) and

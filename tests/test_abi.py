@@ -151,35 +151,35 @@ def test_attention_entry_points_reject_before_launch():
     N = None
     fwd = lambda *a: lib.blockdiag_attn_fwd(*a)  # noqa: E731
     # h_q not a multiple of h_kv
-    assert fwd(1, 1, 64, 0, 64, 6, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 6, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
     # unsupported head_dim
-    assert fwd(1, 1, 64, 0, 64, 4, 4, 60, 0.125, N, N, N, N, N, N, N, 0, N) == 5
-    assert fwd(1, 1, 64, 0, 64, 4, 4, 512, 0.125, N, N, N, N, N, N, N, 0, N) == 5
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 60, 0.125, N, N, N, N, N, N, N, 0, N) == 5
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 512, 0.125, N, N, N, N, N, N, N, 0, N) == 5
     # chunk out of range
-    assert fwd(1, 1, 64, 32, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
+    assert fwd(1, 1, 64, 32, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
     # unknown dtype
-    assert fwd(7, 1, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 5
+    assert fwd(7, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 5
     # null tensors
-    assert fwd(1, 1, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
     # empty chunk is a no-op
-    assert fwd(1, 1, 64, 0, 0, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 0
+    assert fwd(1, 1, 64, 0, 0, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 0
     bwd = lib.blockdiag_attn_bwd
-    assert bwd(1, 1, 64, 0, 64, 6, 4, 64, 0.125, *([N] * 11), 0, N) == 1
+    assert bwd(1, 1, 64, 0, 64, 0, 64, 6, 4, 64, 0.125, *([N] * 11), 0, N) == 1
     # backward workspace too small (checked before anything runs)
     ws = lib.blockdiag_workspace_bytes(1, 1, 1, 64, 64, 4, 4, 64)
     assert ws > 0
     p = 16  # a non-null dummy value; never dereferenced because the check fails first
     m = _desc(1, 64, 0, 64)
-    assert bwd(1, 1, 64, 0, 64, 4, 4, 64, 0.125, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws - 1, N) == 4
+    assert bwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws - 1, N) == 4
     assert b"workspace" in lib.blockdiag_last_error()
     # metadata build rejects an empty table for a non-empty chunk
     desc = bd.MetaDesc()
     cap = lib.blockdiag_meta_ints(1, 64, 64)
-    assert lib.blockdiag_meta_build(p, 0, 1, 64, 0, 64, p, cap, ctypes.byref(desc), N) == 2
+    assert lib.blockdiag_meta_build(p, None, 0, 1, 64, 0, 64, p, cap, ctypes.byref(desc), N) == 2
     assert desc.magic == 0
     # ... a metadata buffer smaller than blockdiag_meta_ints, and a missing descriptor
-    assert lib.blockdiag_meta_build(p, 1, 1, 64, 0, 64, p, cap - 1, ctypes.byref(desc), N) == 3
-    assert lib.blockdiag_meta_build(p, 1, 1, 64, 0, 64, p, cap, None, N) == 1
+    assert lib.blockdiag_meta_build(p, None, 1, 1, 64, 0, 64, p, cap - 1, ctypes.byref(desc), N) == 3
+    assert lib.blockdiag_meta_build(p, None, 1, 1, 64, 0, 64, p, cap, None, N) == 1
     # bounds of rows and keys, then the order of the 32-row query tiles and its two statistics
     assert lib.blockdiag_meta_ints(2, 100, 40) == 2 * 2 * 40 + 2 * 2 * 100 + 2 * 2 + 2
 
@@ -213,11 +213,12 @@ def test_meta_build_host_rejects_before_launch():
     assert desc.magic == bd.META_MAGIC and desc.n_ints == 0
 
 
-def _desc(batch, seq_len, row_offset, q_len, n_ints=None, magic=None, data=16):
+def _desc(batch, seq_len, row_offset, q_len, n_ints=None, magic=None, data=16, kv_lo=0, kv_hi=None):
     lib = bd.load_library()
     m = bd.MetaDesc()
     m.magic = bd.META_MAGIC if magic is None else magic
     m.batch, m.seq_len, m.row_offset, m.q_len = batch, seq_len, row_offset, q_len
+    m.kv_lo, m.kv_hi = kv_lo, row_offset + q_len if kv_hi is None else kv_hi
     m.n_seg = 1
     m.n_ints = lib.blockdiag_meta_ints(batch, seq_len, q_len) if n_ints is None else n_ints
     m.data = data
@@ -233,7 +234,7 @@ def test_attention_rejects_metadata_built_for_other_sizes():
     below is a dummy that a launch would fault on)."""
     lib = bd.load_library()
     p = 16
-    args = (1, 2, 256, 64, 128, 8, 2, 64, 0.125)  # bf16, B=2, S=256, chunk [64, 192)
+    args = (1, 2, 256, 64, 128, 0, 256, 8, 2, 64, 0.125)  # bf16, B=2, S=256, chunk [64, 192), whole-row K/V
     ws = lib.blockdiag_workspace_bytes(1, 1, 2, 256, 128, 8, 2, 64)
     bad = [_desc(2, 256, 64, 64),                  # built for a smaller chunk
            _desc(2, 256, 0, 128),                  # other row_offset
@@ -257,3 +258,37 @@ def test_doc_lens_from_ids():
     assert bd.doc_lens_from_ids([-1, -1]) == []
     with pytest.raises(ValueError):
         bd.doc_lens_from_ids([0, -1, 1])
+
+
+def test_attention_rejects_bad_kv_windows():
+    """K/V windows (kv_begin, kv_len) are checked on the host before any
+    launch: start a multiple of 64, at most row_offset, inside the row,
+    reaching the chunk's end, and holding every key the descriptor says the
+    chunk attends [kv_lo, kv_hi)."""
+    lib = bd.load_library()
+    p = 16
+    B, S, r0, L, Hq, Hkv, d = 1, 512, 256, 128, 4, 1, 64
+    ws = lib.blockdiag_workspace_bytes(1, 1, B, S, L, Hq, Hkv, d)
+    m = _desc(B, S, r0, L, kv_lo=200, kv_hi=384)   # the chunk attends keys [200, 384)
+
+    def fwd(kb, kl):
+        return lib.blockdiag_attn_fwd(1, B, S, r0, L, kb, kl, Hq, Hkv, d, 0.125, p, p, p, ctypes.byref(m), p, p, p,
+                                      0, None)
+
+    def bwd(kb, kl):
+        return lib.blockdiag_attn_bwd(1, B, S, r0, L, kb, kl, Hq, Hkv, d, 0.125, p, p, p, p, p, p, ctypes.byref(m),
+                                      p, p, p, p, ws, None)
+
+    bad = [(100, 284),   # start not a multiple of 64
+           (256, 128),   # starts after key 200, which row 256 attends
+           (-64, 512),   # negative start
+           (128, 200),   # ends at 328 < 384: misses the chunk's end
+           (0, 576),     # past the row
+           (320, 64)]    # after row_offset
+    for kb, kl in bad:
+        assert fwd(kb, kl) == 1, (kb, kl)
+        assert bwd(kb, kl) == 1, (kb, kl)
+    m2 = _desc(B, S, r0, L, kv_lo=200, kv_hi=400)  # attends past the window end
+    assert lib.blockdiag_attn_fwd(1, B, S, r0, L, 192, 192, Hq, Hkv, d, 0.125, p, p, p, ctypes.byref(m2), p, p, p,
+                                  0, None) == 1
+    assert b"misses keys" in lib.blockdiag_last_error()

@@ -14,7 +14,9 @@
 * the launch order does not change a result: the forward and dQ kernels
   run their query tiles longest first when the metadata's statistics say
   so, otherwise in a fixed order; both give the same bits;
-* the autograd wrapper returns the raw calls' results.
+* the autograd wrapper returns the raw calls' results;
+* window-only K/V (the needed-only exchange's buffers, built from the
+  planner's ranges) gives the whole-row call's bits.
 """
 import numpy as np
 import pytest
@@ -175,3 +177,83 @@ def test_autograd_wrapper_matches_raw_calls():
     assert torch.equal(out.detach(), o)
     assert torch.equal(k.grad, dk) and torch.equal(v.grad, dv)
     assert H.rel_fro(q.grad.double().cpu().numpy(), dq.double().cpu().numpy()) < 1e-3
+
+
+WINDOW_CASES = [
+    # (dtype, doc_lens rows, S, cp, rank, h_q, h_kv, d): chunk = rank's rows
+    ("bf16", [[40, 200, 120, 152]], 512, 4, 2, 8, 2, 128),
+    ("bf16", [[300, 20, 100], [64] * 6 + [36]], 448, 2, 1, 8, 2, 64),      # padding tail in row 0
+    ("bf16", [[130, 500, 70, 324]], 1024, 4, 3, 8, 2, 256),
+    ("bf16", [[50, 600, 94]], 768, 8, 6, 4, 2, 96),                         # generic kernels (d = 96)
+    ("f32", [[90, 230, 64, 128]], 512, 2, 1, 4, 4, 64),                     # generic kernels (float32)
+    ("bf16", [[1000, 24]], 1024, 4, 3, 8, 1, 128),                          # all-to-all-v: halo from 3 ranks
+]
+
+
+def _window_inputs(t_full, plan, S):
+    """The K / V a rank holds after the needed-only exchange: its window
+    [kv_begin, kv_end) of every row, filled from the plan's receive ranges
+    and its own chunk, zeros elsewhere."""
+    kb, ke = plan.kv_begin, plan.kv_end
+    C = S // plan.cp
+    r0 = plan.rank * C
+    out = {}
+    for name in ("k", "v"):
+        full = t_full[name]
+        win = np.zeros((full.shape[0], ke - kb) + full.shape[2:], full.dtype)
+        win[:, r0 - kb:ke - kb] = full[:, r0:ke]
+        for (row, _peer, a, e) in plan.recv:
+            win[row, a - kb:e - kb] = full[row, a:e]
+        out[name] = win
+    return out
+
+
+def _run_window(w, t, plan=None):
+    """Whole-row call and window-only call on the same chunk."""
+    import torch
+    import packed_sequence_attention_amd as bd
+    seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device="cuda")
+    d = H.to_device(w, t)
+    o, lse = bd.attn_fwd(d["q"], d["k"], d["v"], seg, w.scale)
+    dq, dk, dv = bd.attn_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], seg, w.scale)
+    tw = _window_inputs(t, plan, w.seq_len)
+    dw = H.to_device(w, tw)
+    ow, lw = bd.attn_fwd(d["q"], dw["k"], dw["v"], seg, w.scale, kv_begin=plan.kv_begin)
+    dqw, dkw, dvw = bd.attn_bwd(d["q"], dw["k"], dw["v"], ow, lw, d["do"], seg, w.scale, kv_begin=plan.kv_begin)
+    torch.cuda.synchronize()
+    return (o, lse, dq, dk, dv), (ow, lw, dqw, dkw, dvw)
+
+
+@gpu
+@pytest.mark.parametrize("case", range(len(WINDOW_CASES) + 1))
+def test_window_only_kv_is_bitwise_whole_row(case):
+    """The needed-only exchange (Automodel page, Summary and Design overview,
+    exchange.py): a rank that holds only its plan's K/V window -- received
+    halo ranges, its own chunk, zeros elsewhere -- gets bit for bit the O,
+    LSE and dQ of the whole-row call, and dK / dV equal to the whole-row
+    call's on the window, which is zero outside it.  The last case is the
+    S = 16384 workload's straddling chunk (rank 2 of 4) at full size."""
+    import torch
+    import packed_sequence_attention_amd as bd
+    if case < len(WINDOW_CASES):
+        dtype, docs, S, cp, rank, hq, hkv, d = WINDOW_CASES[case]
+        C = S // cp
+        w, t = H.small_case(600 + case, dtype, docs, S, rank * C, C, hq, hkv, d)
+        t_full = t
+    else:
+        w = synthetic.workload(3)
+        cp, rank = 4, 2
+        t_full = synthetic.draw_tensors(w)
+        t = t_full
+    plan = bd.kv_plan(w.doc_lens, w.seq_len, cp, rank)
+    print(f"window case {case}: {w.dtype} S={w.seq_len} cp={cp} rank={rank} d={w.head_dim} "
+          f"window=[{plan.kv_begin},{plan.kv_end}) mode={plan.rank_mode}/{plan.step_mode}", flush=True)
+    full, win = _run_window(w, t_full, plan)
+    kb, ke = plan.kv_begin, plan.kv_end
+    for name, a, b in (("o", full[0], win[0]), ("lse", full[1], win[1]), ("dq", full[2], win[2]),
+                       ("dk", full[3][:, kb:ke], win[3]), ("dv", full[4][:, kb:ke], win[4])):
+        assert torch.equal(a, b), f"{name} differs with window-only K/V"
+    assert not full[3][:, :kb].any() and not full[3][:, ke:].any()
+    assert not full[4][:, :kb].any() and not full[4][:, ke:].any()
+    if case == len(WINDOW_CASES) - 1:
+        assert plan.rank_mode == 2  # the 1000-token document spans all four ranks
