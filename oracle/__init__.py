@@ -27,6 +27,13 @@ Modules:
   attention -- dense and windowed fp64 forward (O, LSE) and a hand-derived
                backward (dQ, dK, dV) from the softmax Jacobian.
   brute     -- pure-Python scalar loops for tiny inputs.
+  kvplan    -- reference needed-only K/V exchange plan (halo / all-to-all-v
+               ranges) from the dense mask.
+  dropout   -- attention-dropout keep masks from Philox4x32-10 (the
+               counter-based generator of Salmon et al., SC'11) under a
+               stated counter layout; attention.forward / backward take an
+               optional Dropout.
+  parallel  -- process-pool runner (slicing and reassembly only).
 
 Parity status: every function here is pinned by CPU tests against values
 independent of its own code (torch SDPA as a library special case, closed
@@ -34,4 +41,4 @@ forms, finite differences, brute force, hand-worked fixtures); see the test
 module docstrings.  The bf16 output rounding convention and the padding-row
 convention (O = 0, LSE = -inf) are conventions, not pinned values.
 """
-from . import attention, brute, segment  # noqa: F401
+from . import attention, brute, dropout, kvplan, segment  # noqa: F401

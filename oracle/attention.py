@@ -39,7 +39,35 @@ local query rows (for sampled checks on large workloads).
 """
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
+
+from . import dropout as DR
+
+
+@dataclasses.dataclass(frozen=True)
+class Dropout:
+    """Attention dropout (oracle.dropout): probability p, 64-bit seed and
+    32-bit offset of the generator's counter, and where the arrays passed to
+    forward / backward sit in the full problem -- the query-head count h_q of
+    the full problem, the batch row and query head of their first row and
+    head (b0, h0), and the row position of their key 0 (pos0) -- so a
+    sub-problem draws the same mask as the full one."""
+    p: float
+    seed: int
+    offset: int
+    h_q: int
+    b0: int = 0
+    h0: int = 0
+    pos0: int = 0
+
+    def keep(self, b, h, rows, keys):
+        """(Z, c) for local batch row b, local head h, row / key positions
+        local to the arrays."""
+        z = DR.keep_mask(self.seed, self.offset, self.b0 + b, self.h0 + h, self.h_q,
+                         self.pos0 + np.asarray(rows), self.pos0 + np.asarray(keys), self.p)
+        return z, DR.keep_scale(self.p)[1]
 
 
 def _row_doc_start(lens, seq_len):
@@ -136,9 +164,11 @@ def _check(q, k, v):
     return B, L, Hq, d, S, Hkv, Hq // Hkv
 
 
-def forward(q, k, v, doc_lens_rows, row_offset, scale, block_rows=None, rows=None):
+def forward(q, k, v, doc_lens_rows, row_offset, scale, block_rows=None, rows=None, dropout=None):
     """Returns (o [B,L,Hq,d], lse [B,Hq,L]) in float64.  With ``rows``, only
-    those local rows are computed (others stay O = 0, LSE = -inf)."""
+    those local rows are computed (others stay O = 0, LSE = -inf).  With
+    ``dropout`` (a Dropout), O uses the kept weights P * Z * c; LSE is that
+    of the undropped softmax."""
     B, L, Hq, d, S, Hkv, G = _check(q, k, v)
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
     o = np.zeros((B, L, Hq, d))
@@ -150,15 +180,20 @@ def forward(q, k, v, doc_lens_rows, row_offset, scale, block_rows=None, rows=Non
             g = h // G
             s = scale * (q[b, t0:t1, h, :] @ k[b, w0:w1, g, :].T)
             P, ls = _softmax_block(s, M)
+            if dropout is not None:
+                Z, c = dropout.keep(b, h, np.arange(t0, t1) + row_offset, np.arange(w0, w1))
+                P = P * Z * c
             o[b, t0:t1, h, :] = P @ v[b, w0:w1, g, :]
             lse[b, h, t0:t1] = ls
     return o, lse
 
 
-def backward(q, k, v, do, doc_lens_rows, row_offset, scale, block_rows=None, rows=None):
+def backward(q, k, v, do, doc_lens_rows, row_offset, scale, block_rows=None, rows=None, dropout=None):
     """Returns (dq, dk, dv) in float64 for the loss sum(dO * O).  With
     ``rows``, only those local query rows contribute: their dQ rows are exact,
-    and dK/dV hold the contributions of those rows only."""
+    and dK/dV hold the contributions of those rows only.  With ``dropout``,
+    O = (P * Z * c) V, so dV = (P * Z * c)^T dO and the gradient reaching P
+    is dP = (dO V^T) * Z * c; the softmax Jacobian step is unchanged."""
     B, L, Hq, d, S, Hkv, G = _check(q, k, v)
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64); do = np.asarray(do, np.float64)
@@ -173,11 +208,16 @@ def backward(q, k, v, do, doc_lens_rows, row_offset, scale, block_rows=None, row
             qb, kb, vb, dob = q[b, t0:t1, h], k[b, w0:w1, g], v[b, w0:w1, g], do[b, t0:t1, h]
             P, _ = _softmax_block(scale * (qb @ kb.T), M)
             dP = dob @ vb.T
+            Pv = P  # the weights that multiply V
+            if dropout is not None:
+                Z, c = dropout.keep(b, h, np.arange(t0, t1) + row_offset, np.arange(w0, w1))
+                dP = dP * Z * c
+                Pv = P * Z * c
             r = (P * dP).sum(axis=1)
             dS = P * (dP - r[:, None])
             dq[b, t0:t1, h] = scale * (dS @ kb)
             dk[b, w0:w1, g] += scale * (dS.T @ qb)
-            dv[b, w0:w1, g] += P.T @ dob
+            dv[b, w0:w1, g] += Pv.T @ dob
     return dq, dk, dv
 
 

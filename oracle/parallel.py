@@ -41,12 +41,12 @@ def _limit_threads():
 
 
 def _work(job):
-    idx, kind, b, g, r_a, w0, q, k, v, do, docs, row_offset, scale, block_rows, rows = job
+    idx, kind, b, g, r_a, w0, q, k, v, do, docs, row_offset, scale, block_rows, rows, drop = job
     _limit_threads()
     if kind == "fwd":
-        res = A.forward(q, k, v, docs, row_offset, scale, block_rows=block_rows, rows=rows)
+        res = A.forward(q, k, v, docs, row_offset, scale, block_rows=block_rows, rows=rows, dropout=drop)
     else:
-        res = A.backward(q, k, v, do, docs, row_offset, scale, block_rows=block_rows, rows=rows)
+        res = A.backward(q, k, v, do, docs, row_offset, scale, block_rows=block_rows, rows=rows, dropout=drop)
     return idx, kind, b, g, r_a, w0, res
 
 
@@ -114,13 +114,14 @@ def _pieces(start, row_offset, q_len, rows, n_pieces, align):
 
 
 def run(q, k, v, do, doc_lens_rows, row_offset, scale, block_rows=256, rows=None, workers=None,
-        want=("fwd", "bwd"), pieces=None):
+        want=("fwd", "bwd"), pieces=None, dropout=None):
     """Returns a dict with 'o', 'lse' (if 'fwd' in want) and 'dq', 'dk', 'dv'
     (if 'bwd' in want), all float64, layouts as in oracle.attention.  ``rows``
     restricts the computation to a subset of local rows (as in
     oracle.attention).  ``pieces`` fixes the number of row ranges per (batch
     row, K/V head); by default there are enough for about four jobs per
-    worker."""
+    worker.  ``dropout`` is (p, seed, offset): every job draws the mask of
+    the full problem's batch row, heads and positions."""
     B, L, Hq, d = q.shape
     S, Hkv = k.shape[1], k.shape[2]
     G = Hq // Hkv
@@ -149,13 +150,15 @@ def run(q, k, v, do, doc_lens_rows, row_offset, scale, block_rows=256, rows=None
                 for kind in want:
                     for g in range(Hkv):
                         hs = slice(g * G, (g + 1) * G)
+                        drop = None if dropout is None else A.Dropout(
+                            dropout[0], dropout[1], dropout[2], Hq, b0=b, h0=g * G, pos0=w0)
                         yield (idx, kind, b, g, r_a, w0,
                                np.ascontiguousarray(q[b:b + 1, r_a:r_e, hs]),
                                np.ascontiguousarray(k[b:b + 1, w0:w1, g:g + 1]),
                                np.ascontiguousarray(v[b:b + 1, w0:w1, g:g + 1]),
                                None if (kind == "fwd" or do is None)
                                else np.ascontiguousarray(do[b:b + 1, r_a:r_e, hs]),
-                               docs, ro, scale, block_rows, sub_rows)
+                               docs, ro, scale, block_rows, sub_rows, drop)
                         idx += 1
 
     out = {}
