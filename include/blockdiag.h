@@ -274,6 +274,28 @@ bd_status blockdiag_meta_build_host(const int32_t *h_table, int32_t n_seg, int32
                                     void *stream);
 
 /*
+ * bd_dropout -- attention dropout of the attention calls (Proof section: the
+ * varlen path forwards a dropout probability and the native kernel applies
+ * it).  The pages fix no random-number contract; this one is stated so a
+ * caller (or a reference) can reproduce every mask: the weights that
+ * multiply V are P_ij * Z_ij * c, with Z from Philox4x32-10 (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11).  The pair (query
+ * position i, key position j) -- positions in the packed row, so masks do
+ * not depend on chunking or on the K/V window -- of batch row b and query
+ * head h draws counter (j / 4, i / 4, b * h_q + h, offset) under key
+ * (seed mod 2^32, seed / 2^32); byte j % 4 (least significant first) of
+ * output word i % 4 is kept iff it is >= thr = min(255, round(256 p)), and
+ * kept weights are scaled by c = 256 / (256 - thr) (so the drop rate is
+ * thr / 256).  LSE is that of the undropped softmax.  The backward must get
+ * the forward's p, seed and offset.  A NULL pointer or p = 0 is no dropout.
+ */
+typedef struct bd_dropout {
+  float p;          /* drop probability, 0 <= p < 1                  */
+  uint32_t offset;  /* counter word 3: e.g. layer and step           */
+  uint64_t seed;    /* generator key                                 */
+} bd_dropout;
+
+/*
  * blockdiag_workspace_bytes -- device scratch the forward (is_bwd = 0) or
  * backward (is_bwd = 1) needs for these sizes (0 is a valid answer).
  */
@@ -297,7 +319,8 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
  *   row_offset and q_len (a descriptor built for other sizes, or not built,
  *   is rejected with BD_ERR_INVALID_ARG before any launch); o (device,
  *   dtype) and lse (device, float32) are written in full.
- *   scale multiplies q.k (1/sqrt(head_dim) is the usual choice).
+ *   scale multiplies q.k (1/sqrt(head_dim) is the usual choice); dropout
+ *   (host, may be NULL) as described at bd_dropout.
  *   Supported: any head_dim up to 256 that is a multiple of 8, float32 or
  *   bf16, h_q % h_kv = 0.  bf16 with h_q / h_kv a multiple of 4 runs on the
  *   matrix-core kernels for head_dim 64, 128 and 256 when
@@ -315,7 +338,8 @@ size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t batch, int3
 bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
                              int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
                              int32_t h_kv, int32_t head_dim,
-                             float scale, const void *q, const void *k, const void *v,
+                             float scale, const bd_dropout *dropout, const void *q, const void *k,
+                             const void *v,
                              const bd_meta *meta, void *o, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream);
 
@@ -341,7 +365,8 @@ bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int
 bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
                              int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
                              int32_t h_kv, int32_t head_dim,
-                             float scale, const void *q, const void *k, const void *v,
+                             float scale, const bd_dropout *dropout, const void *q, const void *k,
+                             const void *v,
                              const void *o, const float *lse, const void *d_o,
                              const bd_meta *meta, void *dq, void *dk, void *dv,
                              void *workspace, size_t workspace_bytes, void *stream);
@@ -366,7 +391,8 @@ size_t blockdiag_noalloc_scratch_bytes(void);
 bd_status blockdiag_attn_bwd_noalloc(bd_dtype dtype, int32_t batch, int32_t seq_len,
                                      int32_t row_offset, int32_t q_len, int32_t kv_begin,
                                      int32_t kv_len, int32_t h_q, int32_t h_kv,
-                                     int32_t head_dim, float scale, const void *q, const void *k,
+                                     int32_t head_dim, float scale, const bd_dropout *dropout,
+                                     const void *q, const void *k,
                                      const void *v, const void *o, const float *lse,
                                      const void *d_o, const bd_meta *meta, void *dq, void *dk,
                                      void *dv, void *stream);

@@ -34,7 +34,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "BlockdiagError", "MetaDesc", "SegTable", "segment", "validate", "doc_lens_from_ids",
+    "BlockdiagError", "MetaDesc", "Dropout", "SegTable", "segment", "validate", "doc_lens_from_ids",
     "attn_fwd", "attn_bwd", "attention", "library_path", "load_library", "KvPlan", "kv_plan",
 ]
 
@@ -59,6 +59,21 @@ class MetaDesc(ctypes.Structure):
                 ("row_offset", ctypes.c_int32), ("q_len", ctypes.c_int32), ("n_seg", ctypes.c_int32),
                 ("kv_lo", ctypes.c_int32), ("kv_hi", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("n_ints", ctypes.c_uint64), ("data", ctypes.c_void_p)]
+
+
+class Dropout(ctypes.Structure):
+    """``bd_dropout``: attention dropout of the attention calls (drop
+    probability p, counter offset, 64-bit seed; the mask is a stated
+    function of them, see include/blockdiag.h)."""
+    _fields_ = [("p", ctypes.c_float), ("offset", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+
+
+def _dropout_arg(dropout):
+    """None or (p, seed, offset) -> a bd_dropout pointer (or None)."""
+    if dropout is None:
+        return None
+    p, seed, offset = dropout
+    return ctypes.byref(Dropout(float(p), int(offset) & 0xFFFFFFFF, int(seed) & 0xFFFFFFFFFFFFFFFF))
 
 
 class KvRange(ctypes.Structure):
@@ -112,14 +127,15 @@ def load_library():
     lib.blockdiag_meta_inline_max_seg.restype = i32
     lib.blockdiag_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, i32, i32, i32]
     lib.blockdiag_workspace_bytes.restype = sz
+    pdrop = ctypes.POINTER(Dropout)
     lib.blockdiag_attn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32, i32,
-                                       ctypes.c_float, p, p, p, pdesc, p, p, p, sz, p]
+                                       ctypes.c_float, pdrop, p, p, p, pdesc, p, p, p, sz, p]
     lib.blockdiag_attn_fwd.restype = ctypes.c_int
     lib.blockdiag_attn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32, i32,
-                                       ctypes.c_float, p, p, p, p, p, p, pdesc, p, p, p, p, sz, p]
+                                       ctypes.c_float, pdrop, p, p, p, p, p, p, pdesc, p, p, p, p, sz, p]
     lib.blockdiag_attn_bwd.restype = ctypes.c_int
     lib.blockdiag_attn_bwd_noalloc.argtypes = [ctypes.c_int, i32, i32, i32, i32, i32, i32, i32, i32, i32,
-                                               ctypes.c_float, p, p, p, p, p, p, pdesc, p, p, p, p]
+                                               ctypes.c_float, pdrop, p, p, p, p, p, p, pdesc, p, p, p, p]
     lib.blockdiag_attn_bwd_noalloc.restype = ctypes.c_int
     lib.blockdiag_noalloc_scratch_bytes.argtypes = []
     lib.blockdiag_noalloc_scratch_bytes.restype = sz
@@ -329,10 +345,11 @@ def mark_main_kernel(start_event, stop_event):
     _check(load_library().blockdiag_mark_main_kernel(start_event, stop_event))
 
 
-def attn_fwd(q, k, v, seg, scale=None, kv_begin=0):
+def attn_fwd(q, k, v, seg, scale=None, kv_begin=0, dropout=None):
     """O and LSE of the chunk (``blockdiag_attn_fwd``).  ``k``, ``v`` hold
     keys [kv_begin, kv_begin + k.shape[1]) of every row: the whole row
-    (default) or a window with every key the chunk attends (``kv_plan``)."""
+    (default) or a window with every key the chunk attends (``kv_plan``).
+    ``dropout``: None or (p, seed, offset)."""
     import torch
     lib = load_library()
     B, L, Hq, d, S, Hkv, W = _shapes(q, k, v, seg, kv_begin)
@@ -344,15 +361,17 @@ def attn_fwd(q, k, v, seg, scale=None, kv_begin=0):
     ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):  # the library launches on the current device
-        _check(lib.blockdiag_attn_fwd(dt, B, S, seg.row_offset, L, kv_begin, W, Hq, Hkv, d, scale, q.data_ptr(),
+        _check(lib.blockdiag_attn_fwd(dt, B, S, seg.row_offset, L, kv_begin, W, Hq, Hkv, d, scale,
+                                      _dropout_arg(dropout), q.data_ptr(),
                                       k.data_ptr(), v.data_ptr(), ctypes.byref(seg.desc), o.data_ptr(),
                                       lse.data_ptr(), ws.data_ptr(), ws_bytes, stream))
     return o, lse
 
 
-def attn_bwd(q, k, v, o, lse, do, seg, scale=None, kv_begin=0):
+def attn_bwd(q, k, v, o, lse, do, seg, scale=None, kv_begin=0, dropout=None):
     """dQ, dK, dV of the loss sum(dO * O) (``blockdiag_attn_bwd``); dK, dV
-    cover the same keys as ``k``, ``v``."""
+    cover the same keys as ``k``, ``v``; ``dropout`` as given to the
+    forward."""
     import torch
     lib = load_library()
     B, L, Hq, d, S, Hkv, W = _shapes(q, k, v, seg, kv_begin)
@@ -371,7 +390,8 @@ def attn_bwd(q, k, v, o, lse, do, seg, scale=None, kv_begin=0):
     ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):  # the library launches on the current device
-        _check(lib.blockdiag_attn_bwd(dt, B, S, seg.row_offset, L, kv_begin, W, Hq, Hkv, d, scale, q.data_ptr(),
+        _check(lib.blockdiag_attn_bwd(dt, B, S, seg.row_offset, L, kv_begin, W, Hq, Hkv, d, scale,
+                                      _dropout_arg(dropout), q.data_ptr(),
                                       k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                       do.data_ptr(), ctypes.byref(seg.desc), dq.data_ptr(), dk.data_ptr(),
                                       dv.data_ptr(), ws.data_ptr(), ws_bytes, stream))
@@ -428,19 +448,20 @@ def _autograd_fn():
 
     class _BlockdiagAttention(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, q, k, v, seg, scale, kv_begin):
-            o, lse = attn_fwd(q, k, v, seg, scale, kv_begin)
+        def forward(ctx, q, k, v, seg, scale, kv_begin, dropout):
+            o, lse = attn_fwd(q, k, v, seg, scale, kv_begin, dropout)
             ctx.save_for_backward(q, k, v, o, lse)
             ctx.seg = seg
             ctx.scale = scale
             ctx.kv_begin = kv_begin
+            ctx.dropout = dropout
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.seg, ctx.scale, ctx.kv_begin)
-            return dq, dk, dv, None, None, None
+            dq, dk, dv = attn_bwd(q, k, v, o, lse, do.contiguous(), ctx.seg, ctx.scale, ctx.kv_begin, ctx.dropout)
+            return dq, dk, dv, None, None, None, None
 
     return _BlockdiagAttention
 
@@ -448,11 +469,12 @@ def _autograd_fn():
 _FN = None
 
 
-def attention(q, k, v, seg, scale=None, kv_begin=0):
+def attention(q, k, v, seg, scale=None, kv_begin=0, dropout=None):
     """Drop-in attention over a packed chunk with autograd (Design overview,
     runtime.py: a drop-in SDPA; packed.py: row_offset = 0 for one GPU);
-    ``kv_begin`` as for ``attn_fwd``."""
+    ``kv_begin`` and ``dropout`` (None or (p, seed, offset); the backward
+    reuses the forward's) as for ``attn_fwd``."""
     global _FN
     if _FN is None:
         _FN = _autograd_fn()
-    return _FN.apply(q, k, v, seg, scale, kv_begin)
+    return _FN.apply(q, k, v, seg, scale, kv_begin, dropout)

@@ -66,6 +66,20 @@ bool use_mfma_bwd_full(bd_dtype dtype, int32_t kv_len, int32_t q_len, int32_t he
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Dropout as the kernels take it: the 8-bit threshold round(256 p) (at most
+// 255) and the scale of kept weights 256 / (256 - thr); thr = 0 is none.
+bd_status drop_args(const bd_dropout* d, bd::DropArgs* out) {
+  *out = bd::DropArgs{0, 1.f, 0, 0};
+  if (d == nullptr) return BD_OK;
+  if (!(d->p >= 0.f && d->p < 1.f)) return fail(BD_ERR_INVALID_ARG, "dropout p must be in [0, 1)");
+  const int thr = static_cast<int>(floor(static_cast<double>(d->p) * 256.0 + 0.5));
+  out->thr = static_cast<uint32_t>(thr < 255 ? thr : 255);
+  out->scale = static_cast<float>(256.0 / (256.0 - out->thr));
+  out->seed = d->seed;
+  out->offset = d->offset;
+  return BD_OK;
+}
+
 // O(1) host check that a metadata descriptor was built for this call's sizes
 // (the kernels index the buffer with the call's batch, seq_len and q_len).
 bd_status check_meta(const bd_meta* m, int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len,
@@ -228,8 +242,8 @@ extern "C" size_t blockdiag_workspace_bytes(int is_bwd, bd_dtype dtype, int32_t 
 extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
                                         int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
                                         int32_t h_kv, int32_t head_dim,
-                                        float scale, const void* q, const void* k, const void* v,
-                                        const bd_meta* meta, void* o, float* lse, void* workspace,
+                                        float scale, const bd_dropout* dropout, const void* q, const void* k,
+                                        const void* v, const bd_meta* meta, void* o, float* lse, void* workspace,
                                         size_t workspace_bytes, void* stream) {
   bd::clear_error();
   (void)workspace;
@@ -241,8 +255,11 @@ extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t s
   if (st != BD_OK) return st;
   const size_t need = blockdiag_workspace_bytes(0, dtype, batch, seq_len, q_len, h_q, h_kv, head_dim);
   if (workspace_bytes < need) return fail(BD_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  bd::DropArgs dr;
+  st = drop_args(dropout, &dr);
+  if (st != BD_OK) return st;
   bd::FwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim,
-                scale, q, k, v, meta->data, o, lse, nullptr, nullptr};
+                scale, dr, q, k, v, meta->data, o, lse, nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma_fwd(dtype, kv_len, head_dim, h_q, h_kv, scale) ? bd::launch_fwd_mfma(a, s)
@@ -254,8 +271,8 @@ extern "C" bd_status blockdiag_attn_fwd(bd_dtype dtype, int32_t batch, int32_t s
 extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t row_offset,
                                         int32_t q_len, int32_t kv_begin, int32_t kv_len, int32_t h_q,
                                         int32_t h_kv, int32_t head_dim,
-                                        float scale, const void* q, const void* k, const void* v,
-                                        const void* o, const float* lse, const void* d_o,
+                                        float scale, const bd_dropout* dropout, const void* q, const void* k,
+                                        const void* v, const void* o, const float* lse, const void* d_o,
                                         const bd_meta* meta, void* dq, void* dk, void* dv,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   bd::clear_error();
@@ -278,9 +295,12 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
   }
   st = check_meta(meta, batch, seq_len, row_offset, q_len, kv_begin, kv_len);
   if (st != BD_OK) return st;
+  bd::DropArgs dr;
+  st = drop_args(dropout, &dr);
+  if (st != BD_OK) return st;
   const bool mf = use_mfma_bwd_full(dtype, kv_len, q_len, head_dim, h_q, h_kv, scale);
   bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim, scale,
-                q, k, v, o, lse, d_o, meta->data, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
+                dr, q, k, v, o, lse, d_o, meta->data, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
   take_marks(&a.mark_start, &a.mark_stop);
   hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

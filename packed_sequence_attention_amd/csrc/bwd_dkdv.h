@@ -88,7 +88,7 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, ab);
 }
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
@@ -337,6 +337,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
         const f32x4 st23 = *reinterpret_cast<const f32x4*>(sStat + 2 * r0 + 4);
         const float lsv[4] = {st01[0], st01[2], st23[0], st23[2]};
         const float dev[4] = {st01[1], st01[3], st23[1], st23[3]};
+        // With dropout: the weights that multiply dO are P * Z * c, and the
+        // gradient reaching P is dP = (dO V^T) * Z * c.
+        float zf[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (DROP)
+          keep_factors_col(s.drop, static_cast<uint32_t>(s.row_offset + t0 + r0), static_cast<uint32_t>(key),
+                           static_cast<uint32_t>(b * s.h_q + g * s.group + (it / n_q) * kHW + hsub), zf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = jq * 4 + e;
@@ -345,8 +351,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
             const unsigned rel = static_cast<unsigned>(t0 + r0 + e - mask_lo);
             p = rel < mask_span ? p : 0.f;  // a select: also clears inf on padding rows
           }
-          pv[j] = p;
-          dsv[j] = p * (pacc[j] - dev[e]);
+          pv[j] = DROP ? p * zf[e] : p;
+          dsv[j] = DROP ? p * (pacc[j] * zf[e] - dev[e]) : p * (pacc[j] - dev[e]);
         }
       }
       bf16x8 pb[2], dsb[2];
@@ -515,12 +521,13 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 
 // Launches the dK/dV kernel (the row statistics must already be in
 // a.rowstat: the dQ kernel writes them), bracketed by the profiling marks.
-template <int D>
+template <int D, bool DROP>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   AttnShape s;
   s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
   s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
   s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
+  s.drop = drop_params(a.drop.thr, a.drop.scale, a.drop.seed, a.drop.offset);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int n_kt = (a.kv_len + kKB - 1) / kKB;
   const int n_bg = a.batch * a.h_kv;
@@ -528,7 +535,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   if (n_kt == 0) return hipSuccess;
   hipError_t e = mark(a.mark_start, st);
   if (e != hipSuccess) return e;
-  bwd_dkdv_kernel<D><<<dim3(static_cast<unsigned>(grid)), 512, 0, st>>>(
+  bwd_dkdv_kernel<D, DROP><<<dim3(static_cast<unsigned>(grid)), 512, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.rowstat, m,
       static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg);

@@ -9,6 +9,8 @@
 
 namespace bd {
 
-hipError_t launch_bwd_dkdv64(const BwdArgs& a, hipStream_t st) { return launch_dkdv_t<64>(a, st); }
+hipError_t launch_bwd_dkdv64(const BwdArgs& a, hipStream_t st) {
+  return a.drop.thr != 0 ? launch_dkdv_t<64, true>(a, st) : launch_dkdv_t<64, false>(a, st);
+}
 
 }  // namespace bd

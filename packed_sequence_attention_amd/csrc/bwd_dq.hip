@@ -72,7 +72,7 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, ab);
 }
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ o,
@@ -308,11 +308,22 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
 #pragma unroll
         for (int st_ = 0; st_ < PFT; ++st_) kq[st_] = kread(st_);
         __builtin_amdgcn_sched_barrier(0);
+        // With dropout, the gradient reaching P is dP = (dO V^T) * Z * c.
+        float zf[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) zf[j] = 1.f;
+        if constexpr (DROP) {
+          const uint32_t ip = static_cast<uint32_t>(s.row_offset + qt * kBM + n);
+          const uint32_t bh = static_cast<uint32_t>(b * s.h_q + h);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            keep_factors_row(s.drop, ip, static_cast<uint32_t>(k0 + sb * 32 + g4 * 8 + kg * 4), bh, zf + 4 * g4);
+        }
         float dsv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lse2m));
-          dsv[j] = p * (pacc[j] - dlt);
+          dsv[j] = DROP ? p * (pacc[j] * zf[j] - dlt) : p * (pacc[j] - dlt);
         }
         bf16x8 dsb[2];
 #pragma unroll
@@ -355,17 +366,18 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   }
 }
 
-template <int D>
+template <int D, bool DROP>
 hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
   AttnShape s;
   s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
   s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
   s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
+  s.drop = drop_params(a.drop.thr, a.drop.scale, a.drop.seed, a.drop.offset);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int n_qt = (a.q_len + kBM - 1) / kBM;
   const int n_hg = a.h_q / 4;
   const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
-  bwd_dq_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
+  bwd_dq_kernel<D, DROP><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o),
       static_cast<const uint16_t*>(a.o), a.lse, a.rowstat, m, static_cast<uint16_t*>(a.dq), n_qt, n_hg,
@@ -382,10 +394,11 @@ bool bwd_dq_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim) {
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t st) {
+  const bool drop = a.drop.thr != 0;
   switch (a.head_dim) {
-    case 64: return bwd_dq_t<64>(a, st);
-    case 128: return bwd_dq_t<128>(a, st);
-    case 256: return bwd_dq_t<256>(a, st);
+    case 64: return drop ? bwd_dq_t<64, true>(a, st) : bwd_dq_t<64, false>(a, st);
+    case 128: return drop ? bwd_dq_t<128, true>(a, st) : bwd_dq_t<128, false>(a, st);
+    case 256: return drop ? bwd_dq_t<256, true>(a, st) : bwd_dq_t<256, false>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

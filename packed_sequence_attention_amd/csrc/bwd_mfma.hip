@@ -21,7 +21,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   switch (a.head_dim) {
     case 64: return launch_bwd_dkdv64(a, st);
-    case 128: return launch_dkdv_t<128>(a, st);
+    case 128: return a.drop.thr != 0 ? launch_dkdv_t<128, true>(a, st) : launch_dkdv_t<128, false>(a, st);
     default: return launch_bwd_dkdv256(a, st);
   }
 }

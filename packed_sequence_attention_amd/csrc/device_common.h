@@ -84,6 +84,91 @@ __device__ __forceinline__ int wave_max_i(int x) {
   return __builtin_amdgcn_readfirstlane(x);
 }
 
+// Attention dropout.  Keep decisions come from Philox4x32-10, the
+// counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC'11): ten rounds, each multiplying words 0
+// and 2 of the counter by two fixed 32-bit constants and mixing the high and
+// low product halves with words 1 and 3 and the round key, the key advanced
+// by two Weyl constants between rounds.  The pair (query position i, key
+// position j) of batch row b and query head h -- positions in the packed
+// row, so masks do not depend on chunking or on the K/V window -- reads
+// counter (j / 4, i / 4, b * h_q + h, offset) under key (seed_lo, seed_hi):
+// byte j % 4 of output word i % 4 is kept iff >= thr, and kept weights are
+// multiplied by scale = 256 / (256 - thr).  thr = 0 keeps everything.
+struct DropParams {
+  uint32_t thr;
+  float scale;
+  uint32_t seed_lo, seed_hi, offset;
+};
+
+inline DropParams drop_params(uint32_t thr, float scale, uint64_t seed, uint32_t offset) {
+  DropParams d;
+  d.thr = thr;
+  d.scale = scale;
+  d.seed_lo = static_cast<uint32_t>(seed);
+  d.seed_hi = static_cast<uint32_t>(seed >> 32);
+  d.offset = offset;
+  return d;
+}
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Word w (0..3) of the generator's output for the 4 x 4 block of rows
+// [4 * i4, 4 * i4 + 4) and keys [4 * j4, 4 * j4 + 4) of (b, h); byte e of
+// word w is the draw of (row 4 * i4 + w, key 4 * j4 + e).
+__device__ __forceinline__ uint4 drop_block(const DropParams& dp, uint32_t j4, uint32_t i4, uint32_t bh) {
+  return philox4x32_10(make_uint4(j4, i4, bh, dp.offset), dp.seed_lo, dp.seed_hi);
+}
+__device__ __forceinline__ uint32_t pick_word(uint4 w, int i) {
+  const int s = i & 3;
+  return s == 0 ? w.x : s == 1 ? w.y : s == 2 ? w.z : w.w;
+}
+// The factor a weight is multiplied by: scale if byte e of word is kept, else 0.
+__device__ __forceinline__ float keep_factor(const DropParams& dp, uint32_t word, int e) {
+  return ((word >> (8 * e)) & 0xFFu) >= dp.thr ? dp.scale : 0.f;
+}
+
+// Keep factors of one query position i against the four keys j0 .. j0 + 3
+// (j0 a multiple of 4) of (b, h) -- the layout of a lane that owns a row.
+__device__ __forceinline__ void keep_factors_row(const DropParams& dp, uint32_t i, uint32_t j0, uint32_t bh,
+                                                 float f[4]) {
+  const uint32_t word = pick_word(drop_block(dp, j0 >> 2, i >> 2, bh), static_cast<int>(i));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) f[e] = keep_factor(dp, word, e);
+}
+// Keep factors of the four query positions i0 .. i0 + 3 (any alignment: they
+// may fall in two blocks) against one key position j of (b, h) -- the
+// layout of a lane that owns a key.  i0 % 4 must be the same on every lane
+// (then the second block's draw is a uniform branch).
+__device__ __forceinline__ void keep_factors_col(const DropParams& dp, uint32_t i0, uint32_t j, uint32_t bh,
+                                                 float f[4]) {
+  const uint4 wa = drop_block(dp, j >> 2, i0 >> 2, bh);
+  uint4 wb = wa;
+  if ((i0 & 3u) != 0) wb = drop_block(dp, j >> 2, (i0 >> 2) + 1, bh);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t i = i0 + e;
+    f[e] = keep_factor(dp, pick_word((i >> 2) == (i0 >> 2) ? wa : wb, static_cast<int>(i)), static_cast<int>(j & 3));
+  }
+}
+
+// Keep factor of one (query position i, key position j) pair of (b, h).
+__device__ __forceinline__ float keep_one(const DropParams& dp, uint32_t i, uint32_t j, uint32_t bh) {
+  return keep_factor(dp, pick_word(drop_block(dp, j >> 2, i >> 2, bh), static_cast<int>(i)), static_cast<int>(j & 3));
+}
+
 // Launch parameters.  Sizes are int32 (checked on the host); element
 // offsets are computed in 64-bit.
 struct AttnShape {
@@ -93,6 +178,7 @@ struct AttnShape {
   // kv_begin a multiple of 64 (the whole row: 0 and seq_len).  Positions in
   // the metadata and the masks stay those of the row.
   int kv_begin, kv_len;
+  DropParams drop;  // thr = 0: no dropout
 };
 
 // Query-tile order: the metadata build also writes, for the 32-row query

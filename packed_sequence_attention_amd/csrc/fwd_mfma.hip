@@ -83,7 +83,7 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, ab);
 }
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, MetaView m,
@@ -312,6 +312,19 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
           ps += p[j];
         }
         lrun += ps;
+        if constexpr (DROP) {
+          // dropout of the weights that multiply V (the row sum above is the
+          // undropped one): this lane's row, keys in groups of 4
+          const uint32_t ip = static_cast<uint32_t>(s.row_offset + qt * kBM + n);
+          const uint32_t bh = static_cast<uint32_t>(b * s.h_q + h);
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float f[4];
+            keep_factors_row(s.drop, ip, static_cast<uint32_t>(k0 + sb * 32 + g4 * 8 + kg * 4), bh, f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[g4 * 4 + e] *= f[e];
+          }
+        }
         bf16x8 pb[2];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -362,19 +375,20 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
   }
 }
 
-template <int D>
+template <int D, bool DROP>
 hipError_t fwd_mfma_t(const FwdArgs& a, hipStream_t st) {
   AttnShape s;
   s.batch = a.batch; s.seq_len = a.seq_len; s.row_offset = a.row_offset; s.q_len = a.q_len;
   s.h_q = a.h_q; s.h_kv = a.h_kv; s.head_dim = D; s.group = a.h_q / a.h_kv; s.scale = a.scale;
   s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
+  s.drop = drop_params(a.drop.thr, a.drop.scale, a.drop.seed, a.drop.offset);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int n_qt = (a.q_len + kBM - 1) / kBM;
   const int n_hg = a.h_q / 4;
   const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
   hipError_t e = mark(a.mark_start, st);
   if (e != hipSuccess) return e;
-  fwd_mfma_kernel<D><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
+  fwd_mfma_kernel<D, DROP><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), m, static_cast<uint16_t*>(a.o), a.lse, n_qt, n_hg,
       device_cu_count() * kFwdOcc<D>);
@@ -401,10 +415,11 @@ bool fwd_mfma_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim) {
 }
 
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t st) {
+  const bool drop = a.drop.thr != 0;
   switch (a.head_dim) {
-    case 64: return fwd_mfma_t<64>(a, st);
-    case 128: return fwd_mfma_t<128>(a, st);
-    case 256: return fwd_mfma_t<256>(a, st);
+    case 64: return drop ? fwd_mfma_t<64, true>(a, st) : fwd_mfma_t<64, false>(a, st);
+    case 128: return drop ? fwd_mfma_t<128, true>(a, st) : fwd_mfma_t<128, false>(a, st);
+    case 256: return drop ? fwd_mfma_t<256, true>(a, st) : fwd_mfma_t<256, false>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -96,7 +96,11 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(AttnShape s, const T* 
     const float p = (j < hi) ? expf(sc - mnew) : 0.f;
     const float alpha = expf(mrun - mnew);
     lrun = lrun * alpha + wave_sum(p);
-    sp[wave][lane] = p;
+    // dropout acts on the weights that multiply V, not on the row sum
+    sp[wave][lane] = (s.drop.thr != 0 && j < hi)
+                         ? p * keep_one(s.drop, static_cast<uint32_t>(s.row_offset + t), static_cast<uint32_t>(j),
+                                        static_cast<uint32_t>(b * s.h_q + h))
+                         : p;
     wave_sync();
     const int n = min(64, hi - j0);
 #pragma unroll
@@ -167,7 +171,10 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
     if (j < hi) {
       const int64_t kr = ((kv_base + j) * s.h_kv + g) * D;
       const float p = expf(s.scale * dot_row(sq[wave], k + kr, D) - lse_t);
-      const float dp = dot_row(sdo[wave], v + kr, D);
+      float dp = dot_row(sdo[wave], v + kr, D);
+      if (s.drop.thr != 0)  // the gradient reaching P is (dO . v_j) * Z * c
+        dp *= keep_one(s.drop, static_cast<uint32_t>(s.row_offset + t), static_cast<uint32_t>(j),
+                       static_cast<uint32_t>(b * s.h_q + h));
       ds = p * (dp - delta_t);
     }
     sp[wave][lane] = ds;
@@ -234,8 +241,16 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
         const int64_t row = ((static_cast<int64_t>(b) * s.q_len + t) * s.h_q + h) * D;
         const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
         p = expf(s.scale * dot_row(sk[wave], q + row, D) - lse[st]);
-        const float dp = dot_row(sv[wave], d_o + row, D);
-        ds = p * (dp - rowstat[2 * st + 1]);
+        float dp = dot_row(sv[wave], d_o + row, D);
+        if (s.drop.thr != 0) {  // P * Z * c multiplies dO; the gradient reaching P is dP * Z * c
+          const float z = keep_one(s.drop, static_cast<uint32_t>(s.row_offset + t),
+                                   static_cast<uint32_t>(bj - static_cast<int64_t>(b) * s.seq_len),
+                                   static_cast<uint32_t>(b * s.h_q + h));
+          ds = p * (dp * z - rowstat[2 * st + 1]);
+          p *= z;
+        } else {
+          ds = p * (dp - rowstat[2 * st + 1]);
+        }
       }
       sp[wave][lane] = p;
       sds[wave][lane] = ds;
@@ -313,6 +328,7 @@ AttnShape make_shape(int batch, int seq_len, int row_offset, int q_len, int kv_b
   s.batch = batch; s.seq_len = seq_len; s.row_offset = row_offset; s.q_len = q_len;
   s.h_q = h_q; s.h_kv = h_kv; s.head_dim = head_dim; s.group = h_q / h_kv; s.scale = scale;
   s.kv_begin = kv_begin; s.kv_len = kv_len;
+  s.drop = drop_params(0, 1.f, 0, 0);
   return s;
 }
 
@@ -322,6 +338,7 @@ template <typename T, int NR>
 hipError_t fwd_generic_t(const FwdArgs& a, hipStream_t st) {
   AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.kv_begin, a.kv_len, a.h_q, a.h_kv, a.head_dim,
                            a.scale);
+  s.drop = drop_params(a.drop.thr, a.drop.scale, a.drop.seed, a.drop.offset);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int64_t waves = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
   hipError_t e = mark(a.mark_start, st);
@@ -338,6 +355,7 @@ template <typename T, int NR>
 hipError_t bwd_generic_t(const BwdArgs& a, hipStream_t st) {
   AttnShape s = make_shape(a.batch, a.seq_len, a.row_offset, a.q_len, a.kv_begin, a.kv_len, a.h_q, a.h_kv, a.head_dim,
                            a.scale);
+  s.drop = drop_params(a.drop.thr, a.drop.scale, a.drop.seed, a.drop.offset);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
   const int64_t rows = static_cast<int64_t>(a.batch) * a.q_len * a.h_q;
   const int lpr = lanes_per_row(a.head_dim);

@@ -9,12 +9,21 @@
 
 namespace bd {
 
+// Attention dropout as the kernels take it (thr = 0: none); see DropParams.
+struct DropArgs {
+  uint32_t thr;
+  float scale;
+  uint64_t seed;
+  uint32_t offset;
+};
+
 struct FwdArgs {
   int dtype;  // 0 = f32, 1 = bf16
   int batch, seq_len, row_offset, q_len;
   int kv_begin, kv_len;  // k, v hold keys [kv_begin, kv_begin + kv_len) of every row
   int h_q, h_kv, head_dim;
   float scale;
+  DropArgs drop;
   const void* q;
   const void* k;
   const void* v;
@@ -31,6 +40,7 @@ struct BwdArgs {
   int kv_begin, kv_len;  // k, v, dk, dv hold keys [kv_begin, kv_begin + kv_len) of every row
   int h_q, h_kv, head_dim;
   float scale;
+  DropArgs drop;
   const void* q;
   const void* k;
   const void* v;

@@ -49,7 +49,8 @@ extern "C" size_t blockdiag_noalloc_scratch_bytes(void) { return kScratchBytes; 
 extern "C" bd_status blockdiag_attn_bwd_noalloc(bd_dtype dtype, int32_t batch, int32_t seq_len,
                                                 int32_t row_offset, int32_t q_len, int32_t kv_begin,
                                                 int32_t kv_len, int32_t h_q, int32_t h_kv,
-                                                int32_t head_dim, float scale, const void* q, const void* k,
+                                                int32_t head_dim, float scale, const bd_dropout* dropout,
+                                                const void* q, const void* k,
                                                 const void* v, const void* o, const float* lse, const void* d_o,
                                                 const bd_meta* meta, void* dq, void* dk, void* dv, void* stream) {
   bd::clear_error();
@@ -71,5 +72,5 @@ extern "C" bd_status blockdiag_attn_bwd_noalloc(bd_dtype dtype, int32_t batch, i
     ws_bytes = kScratchBytes;
   }
   return blockdiag_attn_bwd(dtype, batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim, scale,
-                            q, k, v, o, lse, d_o, meta, dq, dk, dv, ws, ws_bytes, stream);
+                            dropout, q, k, v, o, lse, d_o, meta, dq, dk, dv, ws, ws_bytes, stream);
 }

@@ -47,10 +47,10 @@ def run_gpu(w, t, device="cuda", want_bwd=True):
     return {k: v.double().cpu().numpy() for k, v in out.items()}
 
 
-def oracle(w, t, rows=None, want=("fwd", "bwd"), block_rows=256):
+def oracle(w, t, rows=None, want=("fwd", "bwd"), block_rows=256, dropout=None):
     from oracle import parallel
     return parallel.run(t["q"], t["k"], t["v"], t.get("do"), w.doc_lens, w.row_offset, w.scale,
-                        block_rows=block_rows, rows=rows, want=want)
+                        block_rows=block_rows, rows=rows, want=want, dropout=dropout)
 
 
 def lse_diff(a, b):

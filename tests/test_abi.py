@@ -151,26 +151,26 @@ def test_attention_entry_points_reject_before_launch():
     N = None
     fwd = lambda *a: lib.blockdiag_attn_fwd(*a)  # noqa: E731
     # h_q not a multiple of h_kv
-    assert fwd(1, 1, 64, 0, 64, 0, 64, 6, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 6, 4, 64, 0.125, None, N, N, N, N, N, N, N, 0, N) == 1
     # unsupported head_dim
-    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 60, 0.125, N, N, N, N, N, N, N, 0, N) == 5
-    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 512, 0.125, N, N, N, N, N, N, N, 0, N) == 5
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 60, 0.125, None, N, N, N, N, N, N, N, 0, N) == 5
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 512, 0.125, None, N, N, N, N, N, N, N, 0, N) == 5
     # chunk out of range
-    assert fwd(1, 1, 64, 32, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
+    assert fwd(1, 1, 64, 32, 64, 0, 64, 4, 4, 64, 0.125, None, N, N, N, N, N, N, N, 0, N) == 1
     # unknown dtype
-    assert fwd(7, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 5
+    assert fwd(7, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, None, N, N, N, N, N, N, N, 0, N) == 5
     # null tensors
-    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 1
+    assert fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, None, N, N, N, N, N, N, N, 0, N) == 1
     # empty chunk is a no-op
-    assert fwd(1, 1, 64, 0, 0, 0, 64, 4, 4, 64, 0.125, N, N, N, N, N, N, N, 0, N) == 0
+    assert fwd(1, 1, 64, 0, 0, 0, 64, 4, 4, 64, 0.125, None, N, N, N, N, N, N, N, 0, N) == 0
     bwd = lib.blockdiag_attn_bwd
-    assert bwd(1, 1, 64, 0, 64, 0, 64, 6, 4, 64, 0.125, *([N] * 11), 0, N) == 1
+    assert bwd(1, 1, 64, 0, 64, 0, 64, 6, 4, 64, 0.125, None, *([N] * 11), 0, N) == 1
     # backward workspace too small (checked before anything runs)
     ws = lib.blockdiag_workspace_bytes(1, 1, 1, 64, 64, 4, 4, 64)
     assert ws > 0
     p = 16  # a non-null dummy value; never dereferenced because the check fails first
     m = _desc(1, 64, 0, 64)
-    assert bwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws - 1, N) == 4
+    assert bwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, None, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws - 1, N) == 4
     assert b"workspace" in lib.blockdiag_last_error()
     # metadata build rejects an empty table for a non-empty chunk
     desc = bd.MetaDesc()
@@ -244,12 +244,12 @@ def test_attention_rejects_metadata_built_for_other_sizes():
            _desc(2, 256, 64, 128, n_ints=100),     # buffer smaller than the sizes need
            _desc(2, 256, 64, 128, data=None)]      # no buffer
     for m in bad:
-        assert lib.blockdiag_attn_fwd(*args, p, p, p, ctypes.byref(m), p, p, p, 0, None) == 1
+        assert lib.blockdiag_attn_fwd(*args, None, p, p, p, ctypes.byref(m), p, p, p, 0, None) == 1
         assert b"metadata" in lib.blockdiag_last_error()
-        assert lib.blockdiag_attn_bwd(*args, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws, None) == 1
+        assert lib.blockdiag_attn_bwd(*args, None, p, p, p, p, p, p, ctypes.byref(m), p, p, p, p, ws, None) == 1
         assert b"metadata" in lib.blockdiag_last_error()
-    assert lib.blockdiag_attn_fwd(*args, p, p, p, None, p, p, p, 0, None) == 1
-    assert lib.blockdiag_attn_bwd(*args, p, p, p, p, p, p, None, p, p, p, p, ws, None) == 1
+    assert lib.blockdiag_attn_fwd(*args, None, p, p, p, None, p, p, p, 0, None) == 1
+    assert lib.blockdiag_attn_bwd(*args, None, p, p, p, p, p, p, None, p, p, p, p, ws, None) == 1
 
 
 def test_doc_lens_from_ids():
@@ -272,11 +272,11 @@ def test_attention_rejects_bad_kv_windows():
     m = _desc(B, S, r0, L, kv_lo=200, kv_hi=384)   # the chunk attends keys [200, 384)
 
     def fwd(kb, kl):
-        return lib.blockdiag_attn_fwd(1, B, S, r0, L, kb, kl, Hq, Hkv, d, 0.125, p, p, p, ctypes.byref(m), p, p, p,
+        return lib.blockdiag_attn_fwd(1, B, S, r0, L, kb, kl, Hq, Hkv, d, 0.125, None, p, p, p, ctypes.byref(m), p, p, p,
                                       0, None)
 
     def bwd(kb, kl):
-        return lib.blockdiag_attn_bwd(1, B, S, r0, L, kb, kl, Hq, Hkv, d, 0.125, p, p, p, p, p, p, ctypes.byref(m),
+        return lib.blockdiag_attn_bwd(1, B, S, r0, L, kb, kl, Hq, Hkv, d, 0.125, None, p, p, p, p, p, p, ctypes.byref(m),
                                       p, p, p, p, ws, None)
 
     bad = [(100, 284),   # start not a multiple of 64
@@ -289,6 +289,18 @@ def test_attention_rejects_bad_kv_windows():
         assert fwd(kb, kl) == 1, (kb, kl)
         assert bwd(kb, kl) == 1, (kb, kl)
     m2 = _desc(B, S, r0, L, kv_lo=200, kv_hi=400)  # attends past the window end
-    assert lib.blockdiag_attn_fwd(1, B, S, r0, L, 192, 192, Hq, Hkv, d, 0.125, p, p, p, ctypes.byref(m2), p, p, p,
+    assert lib.blockdiag_attn_fwd(1, B, S, r0, L, 192, 192, Hq, Hkv, d, 0.125, None, p, p, p, ctypes.byref(m2), p, p, p,
                                   0, None) == 1
     assert b"misses keys" in lib.blockdiag_last_error()
+
+
+def test_attention_rejects_bad_dropout():
+    """A dropout probability outside [0, 1) (or NaN) is refused on the host."""
+    lib = bd.load_library()
+    p = 16
+    m = _desc(1, 64, 0, 64)
+    for prob in (-0.1, 1.0, 1.5, float("nan")):
+        dr = ctypes.byref(bd.Dropout(prob, 0, 1))
+        assert lib.blockdiag_attn_fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, dr, p, p, p, ctypes.byref(m), p, p,
+                                      p, 0, None) == 1
+        assert b"dropout" in lib.blockdiag_last_error()

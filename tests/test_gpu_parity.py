@@ -402,10 +402,10 @@ def test_binding_rejects_mismatched_tensors_before_launch():
     ws = lib.blockdiag_workspace_bytes(1, 1, 2, 64, 64, 4, 2, 64)
     wsb = torch.empty(ws, dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    code = lib.blockdiag_attn_fwd(1, 2, 64, 0, 64, 0, 64, 4, 2, 64, 0.125, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+    code = lib.blockdiag_attn_fwd(1, 2, 64, 0, 64, 0, 64, 4, 2, 64, 0.125, None, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   ctypes.byref(small.desc), o.data_ptr(), lse.data_ptr(), None, 0, st)
     assert code == 1 and b"metadata" in lib.blockdiag_last_error()
-    code = lib.blockdiag_attn_bwd(1, 2, 64, 0, 64, 0, 64, 4, 2, 64, 0.125, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+    code = lib.blockdiag_attn_bwd(1, 2, 64, 0, 64, 0, 64, 4, 2, 64, 0.125, None, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   o.data_ptr(), lse.data_ptr(), do.data_ptr(), ctypes.byref(small.desc),
                                   do.data_ptr(), k.data_ptr(), v.data_ptr(), wsb.data_ptr(), ws, st)
     assert code == 1 and b"metadata" in lib.blockdiag_last_error()

@@ -33,7 +33,7 @@ def _call_both(w, t):
     dt = 0 if w.dtype == "f32" else 1
     st = torch.cuda.current_stream().cuda_stream
     code = lib.blockdiag_attn_bwd_noalloc(dt, w.batch, w.seq_len, w.row_offset, w.q_len, 0, w.seq_len, w.h_q, w.h_kv,
-                                          w.head_dim, w.scale, d["q"].data_ptr(), d["k"].data_ptr(),
+                                          w.head_dim, w.scale, None, d["q"].data_ptr(), d["k"].data_ptr(),
                                           d["v"].data_ptr(), o.data_ptr(), lse.data_ptr(), d["do"].data_ptr(),
                                           ctypes.byref(seg.desc), outs[0].data_ptr(), outs[1].data_ptr(),
                                           outs[2].data_ptr(), st)
@@ -76,6 +76,6 @@ def test_noalloc_rejects_sizes_past_the_static_scratch():
     m = bd.MetaDesc()
     # batch * q_len * h_q = rows + 32 > rows
     q_len = rows // 32 + 1
-    code = lib.blockdiag_attn_bwd_noalloc(1, 1, q_len, 0, q_len, 0, q_len, 32, 8, 128, 0.088, p, p, p, p, p, p,
+    code = lib.blockdiag_attn_bwd_noalloc(1, 1, q_len, 0, q_len, 0, q_len, 32, 8, 128, 0.088, None, p, p, p, p, p, p,
                                           ctypes.byref(m), p, p, p, None)
     assert code == 4 and b"scratch" in lib.blockdiag_last_error()
