@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--head-dim", type=int, default=None,
                     help="run the named workload's packing and head counts at this head_dim instead "
                          "(e.g. 256); not the headline configuration")
+    ap.add_argument("--h-kv", type=int, default=None,
+                    help="run the named workload's packing with this many K/V heads instead (e.g. 32 for "
+                         "multi-head attention, 16 for GQA 2:1); not the headline configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="also time steps with a buffer of this many MiB written before each one "
@@ -200,6 +203,10 @@ def main():
         w = synthetic.custom_workload(w.wid, w.dtype, w.doc_lens, w.seq_len, w.row_offset, w.q_len, w.h_q,
                                       w.h_kv, args.head_dim,
                                       name=w.name.replace(f"/{w.head_dim}", f"/{args.head_dim}"))
+    if args.h_kv is not None and args.h_kv != w.h_kv:
+        w = synthetic.custom_workload(w.wid, w.dtype, w.doc_lens, w.seq_len, w.row_offset, w.q_len, w.h_q,
+                                      args.h_kv, w.head_dim, w.scale,
+                                      name=w.name.replace(f"/{w.h_kv}/", f"/{args.h_kv}/"))
     t = synthetic.draw_tensors(w)
     dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     d = {k: torch.from_numpy(v).to(dev, dt) for k, v in t.items()}
@@ -307,9 +314,9 @@ def main():
     flops_dkdv = 8 * D * Hq * pairs
     achieved = flops_dkdv / (bwd_avg * 1e-3) / 1e12
     # The kernel the events bracketed: a matrix-core dK/dV kernel (bf16,
-    # head_dim 64 / 128 / 256, GQA ratio a multiple of 4), else the generic
-    # vector-ALU kernel, priced against the fp32 vector peak.
-    on_mfma = w.dtype == "bf16" and D in (64, 128, 256) and (w.h_q // w.h_kv) % 4 == 0
+    # head_dim 64 / 128 / 256, any GQA ratio), else the generic vector-ALU
+    # kernel, priced against the fp32 vector peak.
+    on_mfma = w.dtype == "bf16" and D in (64, 128, 256)
     if on_mfma:
         dkdv_kernel, bound, peak = ("bwd_dkdv256_kernel" if D == 256 else "bwd_dkdv_kernel"), "mfma", PEAK_BF16_TFLOPS
     else:
@@ -323,7 +330,9 @@ def main():
     if flops_dkdv / bytes_dkdv < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
         achieved = bytes_dkdv / (bwd_avg * 1e-3) / 1e9
-    named = args.head_dim is None or args.head_dim == synthetic.workload(args.workload).head_dim
+    base_w = synthetic.workload(args.workload)
+    named = ((args.head_dim is None or args.head_dim == base_w.head_dim)
+             and (args.h_kv is None or args.h_kv == base_w.h_kv))
     traffic = (traffic_from_profile("bwd_dkdv", "bwd_dkdv.h", f"w{args.workload}")
                if on_mfma and D != 256 and named else None)
     out = {

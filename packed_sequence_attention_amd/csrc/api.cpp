@@ -50,12 +50,12 @@ bd_status check_common(bd_dtype dtype, int32_t batch, int32_t seq_len, int32_t r
 }
 
 bool use_mfma_fwd(bd_dtype dtype, int32_t kv_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
-  return bd::mfma_fwd_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f &&
+  return bd::mfma_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f &&
          bd::fwd_mfma_fits(kv_len, h_kv, head_dim);
 }
 
 bool use_mfma_bwd(bd_dtype dtype, int32_t q_len, int32_t head_dim, int32_t h_q, int32_t h_kv, float scale) {
-  return bd::mfma_fwd_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f &&
+  return bd::mfma_supported(static_cast<int>(dtype), head_dim, h_q, h_kv) && scale > 0.f &&
          bd::bwd_mfma_fits(q_len, h_q, head_dim);
 }
 

@@ -21,7 +21,9 @@
 // tiles; splitting their work by head shortens the longest workgroup 4x).
 // Each wave sweeps the 32-row query tiles that attend any of the
 // workgroup's keys ([min key_qlo, max key_qhi) from the per-step metadata),
-// once per group of four heads, and computes for its 32 keys
+// once per group of four heads (for GQA groups of 1 or 2 heads, or not a
+// multiple of 4, the four wave pairs split a head's query tiles instead),
+// and computes for its 32 keys
 // (v_mfma_f32_32x32x16_bf16, lane l: key l % 32):
 //   S = Q K^T and dP = dO V^T   (A = Q / dO rows from LDS, B = K / V in registers)
 //   dV^T += dO^T P, dK^T += Q^T dS  (A = dO^T / Q^T via the LDS transpose
@@ -139,8 +141,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 
   // Q / dO / statistics staging: direct global -> LDS loads (buffer form,
   // so rows past the chunk read as zero) into an LDS double buffer, issued
-  // one iteration ahead.  Iteration it covers the query tile qt0 + it % n_q
-  // of head g*group + (it / n_q)*4 + hsub for the wave pair hsub; of that
+  // one iteration ahead.  Iteration it covers, for the wave pair hsub, the
+  // query tile qt0 + it_tile(it) of head it_head(it) (below); of that
   // pair, key group 0 loads Q, key group 1 loads dO and the row statistics.
   // Q / dO land in the swizzled layout: lane l of a load writes LDS chunk
   // (base + l), so each lane fetches the global chunk that belongs there.
@@ -152,10 +154,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // common to the wave goes into the resource base.
   constexpr int RPL = 64 / CH;  // rows per direct load
   constexpr int PER = 16 / RPL;
-  auto issue_tile = [&](int h, int t0, int buf) {
+  // With live == false (a padding iteration) the loads read nothing and
+  // write zeros; tiles starting past the chunk read zeros as well.
+  auto issue_tile = [&](int h, int t0, int buf, bool live) {
     // row t0 of (b, h); bytes from there to the end of the tensor's rows for this head
     const int64_t tile0 = ((static_cast<int64_t>(b) * s.q_len + t0) * s.h_q + h) * D;
-    const int nbytes = ((s.q_len - t0) * row_stride - h * D) * 2;
+    const int nbytes = live ? max(((s.q_len - t0) * row_stride - h * D) * 2, 0) : 0;
     const uint16_t* src = kgrp == 0 ? q : d_o;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src + tile0), 0, nbytes, 0x00020000);
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     if (kgrp == 1) {  // the tile's (lse * log2(e), delta) pairs: 64 x 4 bytes
       const int64_t st0 = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t0;
       const __amdgpu_buffer_rsrc_t rst = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(rowstat + 2 * st0), 0, (s.q_len - t0) * 8, 0x00020000);
+          const_cast<float*>(rowstat + 2 * st0), 0, live ? max((s.q_len - t0) * 8, 0) : 0, 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rst, (lds_void*)(hb + 2 * kQB * L::QP), 4, lane * 4, 0, 0, 0);
     }
   };
@@ -191,9 +195,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // attends them.  Its loads go out with the K / V / metadata loads (one
   // memory round trip for the prologue instead of two); the metadata only
   // confirms the tile below.
+  // Slot hsub of the four wave pairs: the iteration's heads are hpw heads of
+  // the GQA group (hpw = 4 when the group holds a multiple of 4 heads, 2 for
+  // a multiple of 2, else 1); slot hsub takes head offset hs = hsub % hpw
+  // and query-tile phase ph = hsub / hpw, so with hpw < 4 the slots of one
+  // head split its query tiles tpw = 4 / hpw ways.  Their partial dK / dV
+  // are summed below like those of four heads.
+  const int hpw = heads_per_workgroup(s.group), tpw = kHW / hpw;
+  const int hs = hsub % hpw, ph = hsub / hpw;
   const int qt0e = max(key0 - s.row_offset, 0) / kQB;
   const bool early = qt0e * kQB < s.q_len;
-  if (early) issue_tile(g * s.group + hsub, qt0e * kQB, 0);
+  if (early) issue_tile(g * s.group + hs, (qt0e + ph) * kQB, 0, true);
 
   // K fragments of this wave's keys (B operand of S) in registers; the
   // workgroup's V tile (B operand of dP) in LDS, swizzled like Q / dO.
@@ -248,9 +260,17 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   }
   const int qt0 = gqlo / kQB;
   const int n_q = gqhi > gqlo ? (gqhi - 1) / kQB - qt0 + 1 : 0;
-  const int n_it = n_q * (s.group / kHW);
+  // Iteration it covers heads g * group + (it / n_qp) * hpw + [0, hpw) and,
+  // for slot hsub, query tile qt0 + it_tile(it); a tile index >= n_q pads
+  // the last iteration (its rows lie past every key's row interval, so the
+  // mask zeroes them; the loads write zeros).
+  const int n_qp = (n_q + tpw - 1) / tpw;
+  const int n_it = n_qp * (s.group / hpw);
+  auto it_tile = [&](int it) { return (it % n_qp) * tpw + ph; };
+  auto it_head = [&](int it) { return g * s.group + (it / n_qp) * hpw + hs; };
   auto issue_loads = [&](int it, int buf) {
-    issue_tile(g * s.group + (it / n_q) * kHW + hsub, (qt0 + it % n_q) * kQB, buf);
+    const int ti = it_tile(it);
+    issue_tile(it_head(it), (qt0 + ti) * kQB, buf, ti < n_q);
   };
 
   f32x16 dkacc[DB], dvacc[DB];
@@ -292,7 +312,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // constant and every LDS address is a per-lane base plus an immediate.
   auto step = [&](int it, auto stage) {
     constexpr int buf = decltype(stage)::value;
-    const int t0 = (qt0 + it % n_q) * kQB;
+    const int t0 = (qt0 + it_tile(it)) * kQB;
     const char* sQ = (buf == 0 ? stage0 : stage1) + hsub * L::head;
     const char* sdO = sQ + kQB * L::QP;
     const float* sStat = reinterpret_cast<const float*>(sdO + kQB * L::QP);  // (lse2, delta) pairs
@@ -342,7 +362,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
         float zf[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (DROP)
           keep_factors_col(s.drop, static_cast<uint32_t>(s.row_offset + t0 + r0), static_cast<uint32_t>(key),
-                           static_cast<uint32_t>(b * s.h_q + g * s.group + (it / n_q) * kHW + hsub), zf);
+                           static_cast<uint32_t>(b * s.h_q + it_head(it)), zf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = jq * 4 + e;

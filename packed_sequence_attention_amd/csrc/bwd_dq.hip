@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ o,
     const float* __restrict__ lse, float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dq,
-    int n_qt, int n_hg, int slots) {
+    int n_qtg, int n_hg, int slots, int hpw) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int kBN = kBNd<D>;
@@ -94,12 +94,21 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
 
+  // Work of the workgroup: hpw query heads of one K/V head times
+  // tpw = 4 / hpw consecutive 32-row query tiles (hpw = 4 when the GQA group
+  // has a multiple of 4 heads, 2 for a multiple of 2, else 1): wave w takes
+  // head hg * hpw + w % hpw and tile qtg * tpw + w / hpw.  The four share
+  // every K/V tile staged in LDS and visit the union of their key ranges (a
+  // tile outside a wave's own range is fully masked for it and adds exact
+  // zeros, so a row's result does not depend on its neighbours).
   // Launch order: the last query tiles of the chunk first (neighbouring
   // workgroups share K/V tiles); when the metadata's statistics say the
   // longest tile is long against a slot's share of the work (order_pays),
   // the tiles with the most key tiles to visit first instead (the order the
-  // metadata build sorted).  All n_hg head groups of a tile are adjacent.
-  int qt, b;
+  // metadata build sorted; built for single 32-row tiles, so only used when
+  // tpw = 1).  All n_hg head groups of a tile group are adjacent.
+  const int tpw = 4 / hpw;
+  int qtg, b;
   const int hg = static_cast<int>(blockIdx.x) % n_hg;
   bool sorted = false;
   int code = 0;
@@ -109,16 +118,17 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
                         n_hg, slots);
   }
   if (sorted) {
-    if (code < 0 || code >= s.batch * n_qt) return;  // whole workgroup: no barrier has been reached
-    b = code / n_qt;
-    qt = code % n_qt;
+    if (code < 0 || code >= s.batch * n_qtg) return;  // whole workgroup: no barrier has been reached
+    b = code / n_qtg;
+    qtg = code % n_qtg;
   } else {
     const int per_qt = s.batch * n_hg;
-    qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+    qtg = n_qtg - 1 - static_cast<int>(blockIdx.x) / per_qt;
     b = (static_cast<int>(blockIdx.x) % per_qt) / n_hg;
   }
-  const int h = hg * 4 + wave;
-  const int g = (hg * 4) / s.group;
+  const int qt = qtg * tpw + wave / hpw;
+  const int h = hg * hpw + wave % hpw;
+  const int g = (hg * hpw) / s.group;
 
   const int t = qt * kBM + n;
   const bool valid = t < s.q_len;
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   // loads go out with the prologue loads; a row's dQ depends only on the
   // tiles that are not fully masked for it, summed in descending order
   // whatever the chunk (fully masked tiles add exact zeros).
-  const int kt1 = (s.row_offset + min(qt * kBM + kBM - 1, s.q_len - 1)) / kBN;
+  const int kt1 = (s.row_offset + min((qtg + 1) * tpw * kBM - 1, s.q_len - 1)) / kBN;  // the workgroup's last row
 #pragma unroll
   for (int c = 0; c < 2 * L::NCH; ++c) issue_chunk(kt1, 0, c, true);
   // Keep the metadata reductions below these loads, and the Q loads above
@@ -203,6 +213,19 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   const int lomax = wave_max_i(real ? lo : 0);
   const bool all_real = wave_min_i(real ? 1 : 0) == 1;
   const int pfirst = s.row_offset + qt * kBM;
+  // The key range the workgroup visits: the union over its waves (they
+  // differ only when the waves take different query tiles).
+  int kmin_g = kmin, kmax_g = kmax;
+  if (tpw > 1) {
+    __shared__ int s_rng[2][4];
+    if (lane == 0) {
+      s_rng[0][wave] = kmin;
+      s_rng[1][wave] = kmax;
+    }
+    __syncthreads();
+    kmin_g = __builtin_amdgcn_readfirstlane(min(min(s_rng[0][0], s_rng[0][1]), min(s_rng[0][2], s_rng[0][3])));
+    kmax_g = __builtin_amdgcn_readfirstlane(max(max(s_rng[1][0], s_rng[1][1]), max(s_rng[1][2], s_rng[1][3])));
+  }
 
   // Row statistic delta = dO . O (float32): this lane's half of the row, then
   // the partner lane's.  The (lse * log2(e), delta) pair is also written for
@@ -237,10 +260,10 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
   const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
 
-  if (kmax > kmin) {
+  if (kmax_g > kmin_g) {
     // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked; none before the
     // K/V buffer's first key (clamped as in the forward).
-    const int kt0 = max(kmin, s.kv_begin) / kBN;
+    const int kt0 = max(kmin_g, s.kv_begin) / kBN;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Unrolled by two so that the stage is a compile-time constant.
@@ -374,14 +397,16 @@ hipError_t bwd_dq_t(const BwdArgs& a, hipStream_t st) {
   s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
   s.drop = drop_params(a.drop.thr, a.drop.scale, a.drop.seed, a.drop.offset);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
-  const int n_qt = (a.q_len + kBM - 1) / kBM;
-  const int n_hg = a.h_q / 4;
-  const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
+  const int hpw = heads_per_workgroup(a.h_q / a.h_kv);
+  if (hpw < 4) m.q_order = m.q_stats = nullptr;  // the order is built for single query tiles
+  const int n_qtg = ((a.q_len + kBM - 1) / kBM + 4 / hpw - 1) / (4 / hpw);
+  const int n_hg = a.h_q / hpw;
+  const int64_t grid = static_cast<int64_t>(n_qtg) * a.batch * n_hg;
   bwd_dq_kernel<D, DROP><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o),
-      static_cast<const uint16_t*>(a.o), a.lse, a.rowstat, m, static_cast<uint16_t*>(a.dq), n_qt, n_hg,
-      device_cu_count() * kDqOcc<D>);
+      static_cast<const uint16_t*>(a.o), a.lse, a.rowstat, m, static_cast<uint16_t*>(a.dq), n_qtg, n_hg,
+      device_cu_count() * kDqOcc<D>, hpw);
   return hipGetLastError();
 }
 

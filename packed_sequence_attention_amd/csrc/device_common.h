@@ -207,6 +207,14 @@ __host__ __device__ inline bool order_pays(int max_visits, int total_visits, int
   return 2 * static_cast<int64_t>(max_visits) * slots >= static_cast<int64_t>(total_visits) * head_groups;
 }
 
+// Query heads a matrix-core workgroup takes from one K/V head of a GQA group
+// of `group` heads: 4 when the group holds a multiple of 4 heads, else 2 when
+// it holds a multiple of 2, else 1; its four waves then take 4 / that many
+// consecutive query tiles (forward, dQ) or query-tile phases (dK/dV).
+__host__ __device__ inline int heads_per_workgroup(int group) {
+  return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+}
+
 struct MetaView {
   const int32_t* row_lo;   // [batch][q_len]
   const int32_t* row_hi;   // [batch][q_len]

@@ -88,8 +88,8 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, MetaView m,
                                                           uint16_t* __restrict__ o,
-                                                          float* __restrict__ lse, int n_qt, int n_hg,
-                                                          int slots) {
+                                                          float* __restrict__ lse, int n_qtg, int n_hg,
+                                                          int slots, int hpw) {
   constexpr int KK = D / 16;  // k-steps of Q K^T
   constexpr int DB = D / 32;  // 32-wide blocks of O^T
   constexpr int CH = D / 8;   // 16-byte chunks per K/V row
@@ -105,12 +105,21 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 31, kg = lane >> 5;
 
+  // Work of the workgroup: hpw query heads of one K/V head times
+  // tpw = 4 / hpw consecutive 32-row query tiles (hpw = 4 when the GQA group
+  // has a multiple of 4 heads, 2 for a multiple of 2, else 1): wave w takes
+  // head hg * hpw + w % hpw and tile qtg * tpw + w / hpw.  The four share
+  // every K/V tile staged in LDS and visit the union of their key ranges (a
+  // tile outside a wave's own range is fully masked for it and adds exact
+  // zeros, so a row's result does not depend on its neighbours).
   // Launch order: the last query tiles of the chunk first (neighbouring
   // workgroups share K/V tiles); when the metadata's statistics say the
   // longest tile is long against a slot's share of the work (order_pays),
   // the tiles with the most key tiles to visit first instead (the order the
-  // metadata build sorted).  All n_hg head groups of a tile are adjacent.
-  int qt, b;
+  // metadata build sorted; built for single 32-row tiles, so only used when
+  // tpw = 1).  All n_hg head groups of a tile group are adjacent.
+  const int tpw = 4 / hpw;
+  int qtg, b;
   const int hg = static_cast<int>(blockIdx.x) % n_hg;
   bool sorted = false;
   int code = 0;
@@ -120,16 +129,17 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
                         n_hg, slots);
   }
   if (sorted) {
-    if (code < 0 || code >= s.batch * n_qt) return;  // whole workgroup: no barrier has been reached
-    b = code / n_qt;
-    qt = code % n_qt;
+    if (code < 0 || code >= s.batch * n_qtg) return;  // whole workgroup: no barrier has been reached
+    b = code / n_qtg;
+    qtg = code % n_qtg;
   } else {
     const int per_qt = s.batch * n_hg;
-    qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+    qtg = n_qtg - 1 - static_cast<int>(blockIdx.x) / per_qt;
     b = (static_cast<int>(blockIdx.x) % per_qt) / n_hg;
   }
-  const int h = hg * 4 + wave;
-  const int g = (hg * 4) / s.group;
+  const int qt = qtg * tpw + wave / hpw;
+  const int h = hg * hpw + wave % hpw;
+  const int g = (hg * hpw) / s.group;
 
   const int t = qt * kBM + n;
   const bool valid = t < s.q_len;
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
   // loads go out with the metadata and Q loads; a row's result depends only
   // on the tiles that are not fully masked for it, visited in descending
   // order whatever the chunk (fully masked tiles change nothing).
-  const int kt1 = (s.row_offset + min(qt * kBM + kBM - 1, s.q_len - 1)) / kBN;
+  const int kt1 = (s.row_offset + min((qtg + 1) * tpw * kBM - 1, s.q_len - 1)) / kBN;  // the workgroup's last row
 #pragma unroll
   for (int cc = 0; cc < 2 * L::NCH; ++cc) issue_chunk(kt1, 0, cc, true);
   // Keep the metadata reductions below these loads, and the Q loads above
@@ -208,6 +218,19 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
   const int lomax = wave_max_i(real ? lo : 0);
   const bool all_real = wave_min_i(real ? 1 : 0) == 1;
   const int pfirst = s.row_offset + qt * kBM;
+  // The key range the workgroup visits: the union over its waves (they
+  // differ only when the waves take different query tiles).
+  int kmin_g = kmin, kmax_g = kmax;
+  if (tpw > 1) {
+    __shared__ int s_rng[2][4];
+    if (lane == 0) {
+      s_rng[0][wave] = kmin;
+      s_rng[1][wave] = kmax;
+    }
+    __syncthreads();
+    kmin_g = __builtin_amdgcn_readfirstlane(min(min(s_rng[0][0], s_rng[0][1]), min(s_rng[0][2], s_rng[0][3])));
+    kmax_g = __builtin_amdgcn_readfirstlane(max(max(s_rng[1][0], s_rng[1][1]), max(s_rng[1][2], s_rng[1][3])));
+  }
 
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
@@ -231,11 +254,11 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
     tro[db][1] = (tr_row + 8) * RP + ((chunk ^ rswz<D>(tr_row + 8)) << 4) + half;
   }
 
-  if (kmax > kmin) {
+  if (kmax_g > kmin_g) {
     // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked.  No tile before
     // the K/V buffer's first key is visited (the host checks that the rows'
     // keys lie in the buffer; the clamp keeps a mismatched table in bounds).
-    const int kt0 = max(kmin, s.kv_begin) / kBN;
+    const int kt0 = max(kmin_g, s.kv_begin) / kBN;
     if (!valid) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
@@ -383,15 +406,17 @@ hipError_t fwd_mfma_t(const FwdArgs& a, hipStream_t st) {
   s.kv_begin = a.kv_begin; s.kv_len = a.kv_len;
   s.drop = drop_params(a.drop.thr, a.drop.scale, a.drop.seed, a.drop.offset);
   MetaView m = meta_view(a.meta, a.batch, a.seq_len, a.q_len);
-  const int n_qt = (a.q_len + kBM - 1) / kBM;
-  const int n_hg = a.h_q / 4;
-  const int64_t grid = static_cast<int64_t>(n_qt) * a.batch * n_hg;
+  const int hpw = heads_per_workgroup(a.h_q / a.h_kv);
+  if (hpw < 4) m.q_order = m.q_stats = nullptr;  // the order is built for single query tiles
+  const int n_qtg = ((a.q_len + kBM - 1) / kBM + 4 / hpw - 1) / (4 / hpw);
+  const int n_hg = a.h_q / hpw;
+  const int64_t grid = static_cast<int64_t>(n_qtg) * a.batch * n_hg;
   hipError_t e = mark(a.mark_start, st);
   if (e != hipSuccess) return e;
   fwd_mfma_kernel<D, DROP><<<dim3(static_cast<unsigned>(grid)), 256, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-      static_cast<const uint16_t*>(a.v), m, static_cast<uint16_t*>(a.o), a.lse, n_qt, n_hg,
-      device_cu_count() * kFwdOcc<D>);
+      static_cast<const uint16_t*>(a.v), m, static_cast<uint16_t*>(a.o), a.lse, n_qtg, n_hg,
+      device_cu_count() * kFwdOcc<D>, hpw);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return mark(a.mark_stop, st);
@@ -400,12 +425,7 @@ hipError_t fwd_mfma_t(const FwdArgs& a, hipStream_t st) {
 }  // namespace
 
 bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv) {
-  return dtype == 1 && (head_dim == 64 || head_dim == 128) && h_kv > 0 && h_q % h_kv == 0 &&
-         (h_q / h_kv) % 4 == 0;
-}
-
-bool mfma_fwd_supported(int dtype, int head_dim, int h_q, int h_kv) {
-  return mfma_supported(dtype, head_dim, h_q, h_kv) || (head_dim == 256 && mfma_supported(dtype, 128, h_q, h_kv));
+  return dtype == 1 && (head_dim == 64 || head_dim == 128 || head_dim == 256) && h_kv > 0 && h_q % h_kv == 0;
 }
 
 bool fwd_mfma_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim) {

@@ -73,11 +73,8 @@ int device_cu_count();
 hipError_t launch_fwd_generic(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_generic(const BwdArgs& a, hipStream_t stream);
 
-// bf16 matrix-core kernels: head_dim in {64, 128}, h_q / h_kv a multiple of 4;
+// bf16 matrix-core kernels: head_dim in {64, 128, 256}, any GQA ratio.
 bool mfma_supported(int dtype, int head_dim, int h_q, int h_kv);
-// the same with head_dim 256 as well (forward, dQ and the head_dim-256 dK/dV
-// kernel).
-bool mfma_fwd_supported(int dtype, int head_dim, int h_q, int h_kv);
 // The matrix-core forward addresses a (batch row, K/V head)'s keys (the K/V
 // window) with 31-bit buffer offsets; larger rows take the generic kernel.
 bool fwd_mfma_fits(int64_t kv_len, int64_t h_kv, int64_t head_dim);

@@ -257,3 +257,35 @@ def test_window_only_kv_is_bitwise_whole_row(case):
     assert not full[4][:, :kb].any() and not full[4][:, ke:].any()
     if case == len(WINDOW_CASES) - 1:
         assert plan.rank_mode == 2  # the 1000-token document spans all four ranks
+
+
+@gpu
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (8, 4, 64), (6, 2, 128)])
+def test_chunk_concatenation_any_gqa_ratio(hq, hkv, d):
+    """Query heads from groups of 1, 2 or 3: workgroups of the matrix-core
+    forward and dQ kernels take several query tiles and visit the union of
+    their key ranges; a row's result still depends only on its own tiles, so
+    chunks concatenate bit for bit (O, LSE, dQ) and dK / dV sum to the full
+    call's within tolerance."""
+    import torch
+    import packed_sequence_attention_amd as bd
+    docs = [_w2_small()]
+    S, cp = 2048, 4
+    w, t = H.small_case(250 + hq + d, "bf16", docs, S, 0, S, hq, hkv, d)
+    dd = H.to_device(w, t)
+    full = bd.segment(docs, S, 0, S, device="cuda")
+    o, lse = bd.attn_fwd(dd["q"], dd["k"], dd["v"], full)
+    dq, dk, dv = bd.attn_bwd(dd["q"], dd["k"], dd["v"], o, lse, dd["do"], full)
+    dk_sum = torch.zeros_like(dk, dtype=torch.float32)
+    bounds = [0, 500, 1100, 1600, 2048]   # uneven chunks, not multiples of 32
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        seg = bd.segment(docs, S, a, b - a, device="cuda")
+        qc, doc_ = dd["q"][:, a:b].contiguous(), dd["do"][:, a:b].contiguous()
+        oc, lc = bd.attn_fwd(qc, dd["k"], dd["v"], seg)
+        assert torch.equal(oc, o[:, a:b]) and torch.equal(lc, lse[:, :, a:b])
+        dqc, dkc, _dvc = bd.attn_bwd(qc, dd["k"], dd["v"], oc, lc, doc_, seg)
+        assert torch.equal(dqc, dq[:, a:b])
+        dk_sum += dkc.float()
+    torch.cuda.synchronize()
+    rel = float((dk_sum - dk.float()).norm() / dk.float().norm())
+    assert rel <= 1e-2, rel

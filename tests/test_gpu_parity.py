@@ -187,6 +187,16 @@ SMALL = [
     ("f32", [_rand_docs(13, 200)], 200, 0, 200, 2, 2, 256),
     ("bf16", [_rand_docs(14, 700, hi=400)], 700, 0, 700, 8, 2, 256),
     ("bf16", [[500, 300], [150, 650]], 800, 300, 421, 4, 1, 256),
+    # matrix-core kernels at GQA ratios that are not a multiple of 4: two
+    # heads and two query tiles per workgroup (ratio 2, 6), one head and four
+    # query tiles (ratio 1, 3); ragged tails, chunks, padding, head_dim 256
+    ("bf16", [_rand_docs(15, 900, hi=500)], 900, 0, 900, 8, 8, 128),
+    ("bf16", [_rand_docs(16, 700, fill=650, hi=300), _rand_docs(17, 700)], 700, 77, 555, 8, 4, 128),
+    ("bf16", [_rand_docs(18, 1000, hi=600)], 1000, 200, 700, 6, 2, 64),
+    ("bf16", [_rand_docs(19, 640, hi=200)], 640, 0, 640, 12, 2, 128),
+    ("bf16", [_rand_docs(20, 500, hi=300)], 500, 37, 400, 4, 4, 256),
+    ("bf16", [_rand_docs(21, 600, hi=250)], 600, 0, 600, 4, 2, 256),
+    ("bf16", [[1, 2, 3, 300, 1, 200]], 520, 0, 520, 2, 2, 64),
 ]
 
 
