@@ -34,6 +34,9 @@ Printed: one JSON line (rank 0), with
                 (each tensor touched once) and the HBM rate they imply;
   roofs_us      one step's lower bounds from the matrix-core, HBM and exp
                 roofs next to the measured step;
+  gpu_clock     the engine clock (MHz) read by clock probes launched right
+                after each of ten extra steps; the peaks above assume
+                2.4 GHz;
   flushed       (--flush-mib) the step timed with a buffer written before
                 each one, so inputs come from HBM rather than L2 / the
                 Infinity Cache;
@@ -130,6 +133,27 @@ def traffic_from_profile(kernel, kernel_file, workload_tag):
     return float(m_b.group(1))
 
 
+def observed_clock(bd, step, dev, reps=10, n_wg=64):
+    """The engine clock while the hot path runs: after each of `reps`
+    steps, a clock probe (blockdiag_clock_probe: n_wg one-wave workgroups,
+    each spinning 20 us and counting engine cycles against the 100 MHz
+    real-time counter) on the same stream, while the steps' load still
+    holds the clock.  Returns the median, min and max over all probes (MHz)."""
+    import numpy as np
+    import torch
+    out = torch.zeros(reps, 2 * n_wg, dtype=torch.int64, device=dev)
+    for r in range(reps):
+        step()
+        bd.clock_probe(out[r], ticks=2000)
+    torch.cuda.synchronize()
+    c = out.view(-1, 2).cpu().numpy().astype(np.float64)
+    mhz = c[:, 0] / c[:, 1] * 100.0
+    return {"mhz_median": round(float(np.median(mhz)), 1), "mhz_min": round(float(mhz.min()), 1),
+            "mhz_max": round(float(mhz.max()), 1), "probes": int(mhz.size),
+            "source": "engine cycles / 100 MHz real-time ticks over 20 us, right after each of "
+                      f"{reps} steps"}
+
+
 def cpu_baseline(w, t, flops_per_pair, budget_s=10.0):
     """The fp64 oracle (windowed, unchanged) timed on this host: batch rows
     are run one after another (each row split into (K/V head, query-row
@@ -175,6 +199,9 @@ def main():
                     help="run the named workload's packing with this many K/V heads instead (e.g. 32 for "
                          "multi-head attention, 16 for GQA 2:1); not the headline configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the engine-clock reading")
+    ap.add_argument("--whole-row", action="store_true",
+                    help="pass K/V for the whole row instead of the chunk's K/V window")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="also time steps with a buffer of this many MiB written before each one "
                          "(evicts Q/K/V/dO from L2 and the Infinity Cache; e.g. 512)")
@@ -212,17 +239,33 @@ def main():
     d = {k: torch.from_numpy(v).to(dev, dt) for k, v in t.items()}
     q, k, v, do = d["q"], d["k"], d["v"], d["do"]
     seg0 = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len)
+    # K/V as a context-parallel rank holds them after the needed-only
+    # exchange: keys [kv_begin, row_offset + q_len), kv_begin the first key
+    # any row of the chunk attends rounded down to 64 (the whole row up to
+    # the chunk's end when the chunk starts the row).  --whole-row keeps all
+    # seq_len keys.
+    if args.whole_row:
+        kv_begin, kv_end = 0, w.seq_len
+    else:
+        kv_lo = int(seg0.k_begin.min()) if seg0.n_seg else w.row_offset
+        kv_begin, kv_end = (kv_lo // 64) * 64, w.row_offset + w.q_len
+    k = k[:, kv_begin:kv_end].contiguous()
+    v = v[:, kv_begin:kv_end].contiguous()
+    kv_len = kv_end - kv_begin
     pairs = useful_pairs(seg0)
     D, Hq = w.head_dim, w.h_q
     flops_fwd = 4 * D * Hq * pairs
     flops_bwd = 10 * D * Hq * pairs
-    # Algorithmic HBM bytes (every tensor touched once): W = keys in the
-    # chunk's windows, summed over batch rows (the table's total key length).
+    # Algorithmic HBM bytes (every tensor touched once): K and V are read
+    # over the keys the chunk attends (W, the table's total key length over
+    # the batch rows); dK and dV, outputs over the whole K/V buffer, are
+    # written once (zeros at keys no row attends).
     e_sz = 4 if w.dtype == "f32" else 2
     rows = w.batch * w.q_len
     win = int(seg0.cu_k[seg0.n_seg])
+    kv_keys = w.batch * kv_len
     bytes_fwd = 2 * e_sz * D * Hq * rows + 2 * e_sz * D * w.h_kv * win + 4 * Hq * rows
-    bytes_bwd = 4 * e_sz * D * Hq * rows + 4 * e_sz * D * w.h_kv * win + 8 * Hq * rows
+    bytes_bwd = 4 * e_sz * D * Hq * rows + 2 * e_sz * D * w.h_kv * (win + kv_keys) + 8 * Hq * rows
     exps = 2 * Hq * pairs  # one exp per allowed pair and query head, forward and backward
     ev = HipEvents()
     stream = torch.cuda.current_stream(dev)
@@ -241,10 +284,10 @@ def main():
     # timed in a separate loop below.
     def step(marks=None):
         seg = bd.segment(w.doc_lens, w.seq_len, w.row_offset, w.q_len, device=dev)
-        o, lse = bd.attn_fwd(q, k, v, seg, w.scale)
+        o, lse = bd.attn_fwd(q, k, v, seg, w.scale, kv_begin=kv_begin)
         if marks is not None:
             bd.mark_main_kernel(marks[0], marks[1])
-        dq, dk, dv = bd.attn_bwd(q, k, v, o, lse, do, seg, w.scale)
+        dq, dk, dv = bd.attn_bwd(q, k, v, o, lse, do, seg, w.scale, kv_begin=kv_begin)
         return o, dq
 
     for _ in range(args.warmup):
@@ -276,9 +319,9 @@ def main():
     for _ in range(max(5, args.steps // 2)):
         ev.record(e[0], stream)
         bd.mark_main_kernel(e[3], e[4])
-        o, lse = bd.attn_fwd(q, k, v, seg, w.scale)
+        o, lse = bd.attn_fwd(q, k, v, seg, w.scale, kv_begin=kv_begin)
         ev.record(e[1], stream)
-        bd.attn_bwd(q, k, v, o, lse, do, seg, w.scale)
+        bd.attn_bwd(q, k, v, o, lse, do, seg, w.scale, kv_begin=kv_begin)
         ev.record(e[2], stream)
         torch.cuda.synchronize()
         times_f.append(ev.elapsed_ms(e[0], e[1]))
@@ -325,7 +368,7 @@ def main():
     # once, K, V read and dK, dV written once over the windows.  Below the
     # machine balance (peak FLOP/s over 8 TB/s) the kernel is priced against
     # HBM instead (short documents: few pairs per byte).
-    bytes_dkdv = 2 * e_sz * D * Hq * rows + 4 * e_sz * D * w.h_kv * win + 8 * Hq * rows
+    bytes_dkdv = 2 * e_sz * D * Hq * rows + 2 * e_sz * D * w.h_kv * (win + kv_keys) + 8 * Hq * rows
     unit = "TFLOP/s"
     if flops_dkdv / bytes_dkdv < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
@@ -349,7 +392,7 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "row_offset": w.row_offset,
-                   "q_len": w.q_len, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim,
+                   "q_len": w.q_len, "kv_window": [kv_begin, kv_end], "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.head_dim,
                    "n_docs": w.n_docs, "useful_pairs_per_head": pairs, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_bwd_entry_ms": {"fwd": round(tf, 4), "bwd": round(tb, 4)},
@@ -377,6 +420,8 @@ def main():
     }
     if flushed is not None:
         out["flushed"] = flushed
+    if not args.no_clock:
+        out["gpu_clock"] = observed_clock(bd, step, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, 14 * D)
     print(json.dumps(out), flush=True)

@@ -411,6 +411,21 @@ bd_status blockdiag_attn_bwd_noalloc(bd_dtype dtype, int32_t batch, int32_t seq_
  */
 bd_status blockdiag_mark_main_kernel(void *start_event, void *stop_event);
 
+/*
+ * blockdiag_clock_probe -- measurement aid (not an attention operation):
+ * the engine clock the GPU runs at, for pricing a measured rate against
+ * peaks quoted at 2.4 GHz.  Launches n_workgroups single-wave workgroups on
+ * stream; each spins for `ticks` counts of the constant 100 MHz real-time
+ * counter and writes two uint64 to d_out[2 * w], d_out[2 * w + 1]: the
+ * shader-clock cycles (one per engine clock) and the real-time ticks that
+ * elapsed.  cycles / ticks * 100 is the clock in MHz of the CU that ran
+ * workgroup w.  d_out is device memory of 2 * n_workgroups uint64, owned
+ * by the caller and written asynchronously.  Errors: BD_ERR_INVALID_ARG
+ * (n_workgroups outside 1..65536, ticks outside 1..10^7, NULL d_out),
+ * BD_ERR_HIP.
+ */
+bd_status blockdiag_clock_probe(int32_t n_workgroups, uint32_t ticks, uint64_t *d_out, void *stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char *blockdiag_last_error(void);
 

@@ -48,7 +48,7 @@ EXPORTS = ("blockdiag_segment", "blockdiag_validate", "blockdiag_kv_plan", "bloc
            "blockdiag_meta_build_host", "blockdiag_meta_inline_max_seg",
            "blockdiag_workspace_bytes", "blockdiag_attn_fwd", "blockdiag_attn_bwd",
            "blockdiag_attn_bwd_noalloc", "blockdiag_noalloc_scratch_bytes",
-           "blockdiag_mark_main_kernel", "blockdiag_last_error", "blockdiag_version")
+           "blockdiag_mark_main_kernel", "blockdiag_clock_probe", "blockdiag_last_error", "blockdiag_version")
 
 
 class MetaDesc(ctypes.Structure):
@@ -141,6 +141,8 @@ def load_library():
     lib.blockdiag_noalloc_scratch_bytes.restype = sz
     lib.blockdiag_mark_main_kernel.argtypes = [p, p]
     lib.blockdiag_mark_main_kernel.restype = ctypes.c_int
+    lib.blockdiag_clock_probe.argtypes = [i32, ctypes.c_uint32, p, p]
+    lib.blockdiag_clock_probe.restype = ctypes.c_int
     lib.blockdiag_last_error.argtypes = []
     lib.blockdiag_last_error.restype = ctypes.c_char_p
     lib.blockdiag_version.argtypes = []
@@ -343,6 +345,19 @@ def mark_main_kernel(start_event, stop_event):
     attn_bwd call records these hipEvent_t handles (ints) around its main
     kernel on its stream."""
     _check(load_library().blockdiag_mark_main_kernel(start_event, stop_event))
+
+
+def clock_probe(out, ticks=2000, stream=None):
+    """Measurement aid (``blockdiag_clock_probe``): launches out.numel() // 2
+    one-wave workgroups that spin ``ticks`` counts of the 100 MHz real-time
+    counter; ``out`` (int64, on the GPU) receives (engine cycles, ticks) per
+    workgroup.  Returns nothing; read ``out`` after the stream has run."""
+    import torch
+    if out.dtype != torch.int64 or not out.is_cuda or not out.is_contiguous() or out.numel() < 2:
+        raise BlockdiagError(1, "clock_probe needs a contiguous int64 CUDA tensor of at least 2 elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device)
+    _check(load_library().blockdiag_clock_probe(out.numel() // 2, ticks, out.data_ptr(), stream.cuda_stream))
 
 
 def attn_fwd(q, k, v, seg, scale=None, kv_begin=0, dropout=None):

@@ -304,3 +304,16 @@ def test_attention_rejects_bad_dropout():
         assert lib.blockdiag_attn_fwd(1, 1, 64, 0, 64, 0, 64, 4, 4, 64, 0.125, dr, p, p, p, ctypes.byref(m), p, p,
                                       p, 0, None) == 1
         assert b"dropout" in lib.blockdiag_last_error()
+
+
+def test_clock_probe_rejects_before_launch():
+    """The clock probe checks its arguments on the host and launches
+    nothing when they fail."""
+    lib = bd.load_library()
+    p = 16
+    assert lib.blockdiag_clock_probe(0, 2000, p, None) == 1
+    assert lib.blockdiag_clock_probe(65537, 2000, p, None) == 1
+    assert lib.blockdiag_clock_probe(8, 0, p, None) == 1
+    assert lib.blockdiag_clock_probe(8, 10000001, p, None) == 1
+    assert lib.blockdiag_clock_probe(8, 2000, None, None) == 1
+    assert b"clock_probe" in lib.blockdiag_last_error()
