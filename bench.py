@@ -15,21 +15,25 @@ workload is bf16 B=2, S=4096 per row, H_q=32, H_kv=8, d=128, lognormal
 document lengths (median 512), row_offset 0.
 
 Printed: one JSON line (rank 0), with
-  roofline      the backward's dK/dV kernel (the dominant one): algorithmic
-                FLOP per launch (the four products S, dP, dV, dK at 2*d FLOP
-                per allowed pair and query head each; the backward's fifth,
-                dQ, is credited to the dQ kernel and its recomputation of S
-                and dP is not counted) / its mean duration from HIP events
-                recorded around that kernel on its stream in ten of the timed
-                steps (spread over the timed region), against the bf16
-                dense matrix-core peak (the fp32 vector-ALU peak, bound "alu",
-                for shapes on the generic kernels, e.g. the float32
+  roofline      the backward's main kernel: the short-document kernel
+                (dQ, dK and dV in one pass; taken when no segment has more
+                than 128 keys, bf16, head_dim 64 / 128) or else the dK/dV
+                kernel (the dominant one of the tile kernels).  achieved =
+                algorithmic FLOP per launch (short-document kernel: all
+                five products, 10 * d FLOP per allowed pair and query head;
+                dK/dV kernel: the four products S, dP, dV, dK, 8 * d -- dQ
+                is credited to the dQ kernel and its recomputation of S and
+                dP is not counted) / its mean duration from HIP events
+                recorded around that kernel on its stream in ten of the
+                timed steps (spread over the timed region), against the bf16
+                dense matrix-core peak (the fp32 vector-ALU peak, bound
+                "alu", for shapes on the generic kernels, e.g. the float32
                 workload 1); where that kernel's FLOP per algorithmic byte
                 is below the machine balance (short documents, e.g. the
-                fragmented S=49152 workload) it is priced in GB/s against the
-                8 TB/s HBM peak instead (bound "hbm"); `traffic` from the committed rocprofv3
-                counter summary when it was taken on the current kernel
-                source, else null;
+                fragmented S=49152 workload) it is priced in GB/s against
+                the 8 TB/s HBM peak instead (bound "hbm"); `traffic` from
+                the committed rocprofv3 counter summary when it was taken on
+                the current kernel source, else null;
   hbm           algorithmic bytes of the forward and backward entry points
                 (each tensor touched once) and the HBM rate they imply;
   roofs_us      one step's lower bounds from the matrix-core, HBM and exp
@@ -247,7 +251,10 @@ def main():
     if args.whole_row:
         kv_begin, kv_end = 0, w.seq_len
     else:
-        kv_lo = int(seg0.k_begin.min()) if seg0.n_seg else w.row_offset
+        # first key position attended in any batch row (non-padding segments)
+        real = np.diff(seg0.cu_k) > 0
+        pos = seg0.k_begin - (seg0.cu_q[:-1] // max(w.q_len, 1)) * w.seq_len
+        kv_lo = int(pos[real].min()) if real.any() else w.row_offset
         kv_begin, kv_end = (kv_lo // 64) * 64, w.row_offset + w.q_len
     k = k[:, kv_begin:kv_end].contiguous()
     v = v[:, kv_begin:kv_end].contiguous()
@@ -354,29 +361,47 @@ def main():
                    "hbm_gbs": round((bytes_fwd + bytes_bwd) / (tfl * 1e-3) / 1e9, 1)}
 
     value = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
-    flops_dkdv = 8 * D * Hq * pairs
-    achieved = flops_dkdv / (bwd_avg * 1e-3) / 1e12
-    # The kernel the events bracketed: a matrix-core dK/dV kernel (bf16,
-    # head_dim 64 / 128 / 256, any GQA ratio), else the generic vector-ALU
-    # kernel, priced against the fp32 vector peak.
+    # The kernel the events bracketed (the backward's main kernel): for
+    # packings of short documents (bf16, head_dim 64 / 128, no segment of
+    # more than 128 keys, at most 2047 segments) the short-document kernel,
+    # which computes dQ, dK and dV in one pass; else a matrix-core dK/dV
+    # kernel (bf16, head_dim 64 / 128 / 256, any GQA ratio); else the generic
+    # vector-ALU kernel, priced against the fp32 vector peak.
+    short_path = (w.dtype == "bf16" and D in (64, 128) and 0 <= seg0.max_k <= 128 and seg0.n_seg <= 2047)
     on_mfma = w.dtype == "bf16" and D in (64, 128, 256)
-    if on_mfma:
-        dkdv_kernel, bound, peak = ("bwd_dkdv256_kernel" if D == 256 else "bwd_dkdv_kernel"), "mfma", PEAK_BF16_TFLOPS
+    if short_path:
+        # all five products, each pair once: 10 * d FLOP per pair and head
+        main_kernel, main_src, main_tag, bound, peak = "bwd_short_kernel", "bwd_short.hip", "bwd_short", "mfma", \
+            PEAK_BF16_TFLOPS
+        flops_main = 10 * D * Hq * pairs
+        # Q, dO, O read and dQ written once, lse read; K, V read over the
+        # attended keys; dK, dV written over the whole K/V buffer
+        bytes_main = 4 * e_sz * D * Hq * rows + 2 * e_sz * D * w.h_kv * (win + kv_keys) + 4 * Hq * rows
     else:
-        dkdv_kernel, bound, peak = "dkv_generic_kernel", "alu", PEAK_FP32_VALU_TFLOPS
-    # The dK/dV kernel's algorithmic bytes: Q, dO and the row statistics read
-    # once, K, V read and dK, dV written once over the windows.  Below the
-    # machine balance (peak FLOP/s over 8 TB/s) the kernel is priced against
-    # HBM instead (short documents: few pairs per byte).
-    bytes_dkdv = 2 * e_sz * D * Hq * rows + 2 * e_sz * D * w.h_kv * (win + kv_keys) + 8 * Hq * rows
+        # the four products S, dP, dV, dK at 2 * d FLOP per pair and query
+        # head each (the backward's fifth, dQ, is credited to the dQ kernel
+        # and its recomputation of S and dP is not counted)
+        if on_mfma:
+            main_kernel, bound, peak = ("bwd_dkdv256_kernel" if D == 256 else "bwd_dkdv_kernel"), "mfma", \
+                PEAK_BF16_TFLOPS
+        else:
+            main_kernel, bound, peak = "dkv_generic_kernel", "alu", PEAK_FP32_VALU_TFLOPS
+        main_src, main_tag = "bwd_dkdv.h", "bwd_dkdv"
+        flops_main = 8 * D * Hq * pairs
+        # Q, dO and the row statistics read once, K, V read and dK, dV
+        # written once over the windows
+        bytes_main = 2 * e_sz * D * Hq * rows + 2 * e_sz * D * w.h_kv * (win + kv_keys) + 8 * Hq * rows
+    achieved = flops_main / (bwd_avg * 1e-3) / 1e12
+    # Below the machine balance (peak FLOP/s over 8 TB/s) the kernel is
+    # priced against HBM instead (short documents: few pairs per byte).
     unit = "TFLOP/s"
-    if flops_dkdv / bytes_dkdv < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+    if flops_main / bytes_main < peak * 1e12 / (PEAK_HBM_GBS * 1e9):
         bound, peak, unit = "hbm", PEAK_HBM_GBS, "GB/s"
-        achieved = bytes_dkdv / (bwd_avg * 1e-3) / 1e9
+        achieved = bytes_main / (bwd_avg * 1e-3) / 1e9
     base_w = synthetic.workload(args.workload)
     named = ((args.head_dim is None or args.head_dim == base_w.head_dim)
              and (args.h_kv is None or args.h_kv == base_w.h_kv))
-    traffic = (traffic_from_profile("bwd_dkdv", "bwd_dkdv.h", f"w{args.workload}")
+    traffic = (traffic_from_profile(main_tag, main_src, f"w{args.workload}")
                if on_mfma and D != 256 and named else None)
     out = {
         "metric": METRIC,
@@ -397,7 +422,7 @@ def main():
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_bwd_entry_ms": {"fwd": round(tf, 4), "bwd": round(tb, 4)},
         "tflops_fwd_plus_bwd_calls": round((flops_fwd + flops_bwd) / ((tf + tb) * 1e-3) / 1e12, 3),
-        "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd_dkdv": round(bwd_avg, 4)},
+        "main_kernel_ms": {"fwd": round(fwd_avg, 4), "bwd_main": round(bwd_avg, 4)},
         "fwd_kernel_tflops": round(flops_fwd / (fwd_avg * 1e-3) / 1e12, 3),
         # Algorithmic HBM bytes of each entry point and the rate they imply at
         # the entry points' event times, against the 8 TB/s HBM peak.
@@ -413,9 +438,9 @@ def main():
                      "hbm": round((bytes_fwd + bytes_bwd) / (PEAK_HBM_GBS * 1e9) * 1e6, 2),
                      "exp": round(exps / PEAK_EXP_PER_S * 1e6, 2),
                      "step": round(ms_per_step * 1e3, 2)},
-        "roofline": {"bound": bound, "kernel": dkdv_kernel, "achieved": round(achieved, 3),
+        "roofline": {"bound": bound, "kernel": main_kernel, "achieved": round(achieved, 3),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "algorithmic_flop": flops_dkdv, "algorithmic_bytes": bytes_dkdv,
+                     "algorithmic_flop": flops_main, "algorithmic_bytes": bytes_main,
                      "traffic": traffic, "launches_timed": len(bwd_ms)},
     }
     if flushed is not None:

@@ -197,7 +197,7 @@ typedef struct bd_meta {
   int32_t n_seg;        /* segments of the table it was built from         */
   int32_t kv_lo;        /* keys the chunk attends, over all batch rows:    */
   int32_t kv_hi;        /*   [kv_lo, kv_hi) (kv_lo = 0 when unknown)       */
-  int32_t reserved;
+  int32_t max_seg_k;    /* most keys of one segment (-1 when unknown)      */
   uint64_t n_ints;      /* int32 entries written: blockdiag_meta_ints(...) */
   const int32_t *data;  /* the device buffer (caller-owned)                */
 } bd_meta;
@@ -205,7 +205,9 @@ typedef struct bd_meta {
 /*
  * blockdiag_meta_ints -- number of int32 in the device metadata buffer that
  * blockdiag_meta_build fills: 2 * batch * q_len + 2 * batch * seq_len,
- * plus nq + 2 with nq = batch * ceil(q_len / 32) when 1 <= nq <= 8192.
+ * plus nq + 2 with nq = batch * ceil(q_len / 32) when 1 <= nq <= 8192,
+ * plus 1 + 3 * nb with nb = batch * (2 * ceil((q_len + 127) / 128) + 1)
+ * when batch * q_len > 0.
  *
  * blockdiag_meta_build -- expands a validated segment table (device copy)
  * into per-row and per-key mask bounds on the device, once per step, so the
@@ -235,14 +237,27 @@ typedef struct bd_meta {
  *               the largest visit count is at least half of one workgroup
  *               slot's share of the total (then the launch order sets the
  *               tail), otherwise last tiles first; results do not depend on
- *               the order.
+ *               the order.  Absent (no entries) for more than 8192 tiles.
+ *             bins[1 + 3 * nb]: the short-document bins.  bins[0] is their
+ *               count, then per bin the first and one-past-last local row
+ *               (flattened [batch * q_len] index) and the flattened key
+ *               index (b * seq_len + position) of its first key; its keys
+ *               end one past its last row's position.  Consecutive
+ *               documents of one batch row are grouped greedily in table
+ *               order while the group's keys span at most 128 positions; a
+ *               padding segment or a new batch row starts a new bin.  Built
+ *               only when no segment has more than 128 keys (else the count
+ *               is 0); every row of a document and every key it attends then
+ *               lies in exactly one bin.
  *   desc      (host, required) receives the buffer's descriptor for the
  *             attention calls; on any error its magic is set to 0.
  *   h_table   (host, optional) the same table in host memory: the
  *             descriptor then records the key window the chunk attends
  *             (kv_lo, kv_hi), which a window-only K/V call is checked
- *             against.  NULL records kv_lo = 0, kv_hi = row_offset + q_len,
- *             so only K/V windows starting at key 0 are accepted.
+ *             against, and the most keys of one segment (max_seg_k), by
+ *             which the backward picks its short-document kernel.  NULL
+ *             records kv_lo = 0, kv_hi = row_offset + q_len (so only K/V
+ *             windows starting at key 0 are accepted) and max_seg_k = -1.
  * The table is not re-validated here (that needs a sync); the kernel clamps
  * every bound to its row so a corrupt table cannot make later kernels read
  * out of bounds.  Errors: BD_ERR_INVALID_ARG, BD_ERR_CAPACITY (meta_capacity

@@ -57,7 +57,7 @@ class MetaDesc(ctypes.Structure):
     the buffer was built for (the attention calls check them)."""
     _fields_ = [("magic", ctypes.c_uint32), ("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
                 ("row_offset", ctypes.c_int32), ("q_len", ctypes.c_int32), ("n_seg", ctypes.c_int32),
-                ("kv_lo", ctypes.c_int32), ("kv_hi", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("kv_lo", ctypes.c_int32), ("kv_hi", ctypes.c_int32), ("max_seg_k", ctypes.c_int32),
                 ("n_ints", ctypes.c_uint64), ("data", ctypes.c_void_p)]
 
 

@@ -152,10 +152,19 @@ void table_window(const int32_t* h_table, int32_t n_seg, int32_t seq_len, int32_
   *hi = static_cast<int32_t>(whi);
 }
 
+// Most keys of one segment of a host table (-1 without the table).
+int32_t table_max_seg_k(const int32_t* h_table, int32_t n_seg) {
+  if (h_table == nullptr) return -1;
+  const int32_t* cu_k = h_table + n_seg + 1;
+  int32_t mx = 0;
+  for (int32_t s = 0; s < n_seg; ++s) mx = cu_k[s + 1] - cu_k[s] > mx ? cu_k[s + 1] - cu_k[s] : mx;
+  return mx;
+}
+
 void fill_desc(bd_meta* desc, int32_t n_seg, int32_t batch, int32_t seq_len, int32_t row_offset, int32_t q_len,
                const int32_t* d_meta, const int32_t* h_table) {
   table_window(h_table, n_seg, seq_len, row_offset, q_len, &desc->kv_lo, &desc->kv_hi);
-  desc->reserved = 0;
+  desc->max_seg_k = table_max_seg_k(h_table, n_seg);
   desc->batch = batch;
   desc->seq_len = seq_len;
   desc->row_offset = row_offset;
@@ -189,9 +198,9 @@ extern "C" bd_status blockdiag_mark_main_kernel(void* start_event, void* stop_ev
 
 extern "C" size_t blockdiag_meta_ints(int32_t batch, int32_t seq_len, int32_t q_len) {
   if (batch < 0 || seq_len < 0 || q_len < 0) return 0;
-  // row bounds, key bounds, then the query- and key-tile orders
+  // row bounds, key bounds, then the query-tile order and the short-document bins
   return 2 * static_cast<size_t>(batch) * q_len + 2 * static_cast<size_t>(batch) * seq_len +
-         bd::meta_order_ints(batch, seq_len, q_len);
+         bd::meta_tail_ints(batch, seq_len, q_len);
 }
 
 extern "C" bd_status blockdiag_meta_build(const int32_t* d_table, const int32_t* h_table, int32_t n_seg,
@@ -301,6 +310,8 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
   const bool mf = use_mfma_bwd_full(dtype, kv_len, q_len, head_dim, h_q, h_kv, scale);
   bd::BwdArgs a{static_cast<int>(dtype), batch, seq_len, row_offset, q_len, kv_begin, kv_len, h_q, h_kv, head_dim, scale,
                 dr, q, k, v, o, lse, d_o, meta->data, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
+  a.n_seg = meta->n_seg;
+  a.max_seg_k = meta->max_seg_k;
   take_marks(&a.mark_start, &a.mark_stop);
   hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

@@ -215,6 +215,31 @@ __host__ __device__ inline int heads_per_workgroup(int group) {
   return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
 }
 
+// Short-document bins: consecutive documents (non-padding segments) of one
+// batch row grouped greedily, in table order, so that each group's keys span
+// at most kBinCap positions.  Built only when every segment has at most
+// kBinCap keys and the table at most kBinMaxSeg segments; then every local row of a document and every key it attends
+// belong to exactly one bin, and the short-document backward takes a bin
+// per workgroup.  A bin is (first row, end row) of the flattened
+// [batch * q_len] rows and the flattened key index (b * seq_len + position)
+// of its first key; its keys end one past its last row's position.  Per
+// batch row, two consecutive bins hold more than kBinCap keys together (the
+// second one's first document did not fit the first) and the row's bins
+// hold at most q_len + kBinCap - 1 keys (only the chunk's first document
+// has keys before the chunk, fewer than kBinCap), which bounds the count.
+constexpr int kBinCap = 128;
+// Bins are built for tables of at most this many segments (the builder
+// stages the table in LDS); longer tables get none.
+constexpr int kBinMaxSeg = 2047;
+__host__ __device__ inline int64_t max_bins(int batch, int q_len) {
+  return static_cast<int64_t>(batch) * (2 * ((static_cast<int64_t>(q_len) + 2 * kBinCap - 2) / kBinCap) + 1);
+}
+// int32 entries of the bin section: the count, then 3 per bin (none for an
+// empty chunk).
+__host__ __device__ inline int64_t meta_bin_ints(int batch, int q_len) {
+  return static_cast<int64_t>(batch) * q_len > 0 ? 1 + 3 * max_bins(batch, q_len) : 0;
+}
+
 struct MetaView {
   const int32_t* row_lo;   // [batch][q_len]
   const int32_t* row_hi;   // [batch][q_len]
@@ -222,6 +247,7 @@ struct MetaView {
   const int32_t* key_qhi;  // [batch][seq_len]
   const int32_t* q_order;  // [batch * n_qt] tile codes, most visits first (null: not built)
   const int32_t* q_stats;  // [2] largest and total visits (null: not built)
+  const int32_t* bins;     // [0]: bin count (0: not built), then (row begin, row end, first key) per bin
 };
 
 __host__ __device__ inline MetaView meta_view(const int32_t* meta, int batch, int seq_len, int q_len) {
@@ -235,6 +261,7 @@ __host__ __device__ inline MetaView meta_view(const int32_t* meta, int batch, in
   const bool ord = order_built(batch, q_len);
   m.q_order = ord ? meta + 2 * nr + 2 * nk : nullptr;
   m.q_stats = ord ? m.q_order + order_q_tiles(batch, q_len) : nullptr;
+  m.bins = meta + 2 * nr + 2 * nk + (ord ? order_q_tiles(batch, q_len) + 2 : 0);
   return m;
 }
 

@@ -54,6 +54,8 @@ struct BwdArgs {
   float* rowstat;  // workspace: [batch][h_q][q_len] pairs (lse * log2(e), delta)
   hipEvent_t mark_start;  // recorded around the main kernel when non-null
   hipEvent_t mark_stop;
+  int n_seg = 0;        // segments of the table the metadata was built from
+  int max_seg_k = -1;   // most keys of one segment (-1: unknown)
 };
 
 // Metadata expansion (segment table -> per-row / per-key bounds).  With
@@ -63,9 +65,9 @@ constexpr int kInlineSeg = 126;
 constexpr int kInlineTableInts = 3 * kInlineSeg + 2;
 hipError_t launch_meta_build(const int32_t* table, bool host_table, int n_seg, int batch, int seq_len,
                              int row_offset, int q_len, int32_t* d_meta, hipStream_t stream);
-// int32 entries of the query-tile order and its statistics that follow the
-// bounds in the metadata buffer.
-size_t meta_order_ints(int batch, int seq_len, int q_len);
+// int32 entries that follow the bounds in the metadata buffer: the
+// query-tile order and its statistics (when built), then the bins.
+size_t meta_tail_ints(int batch, int seq_len, int q_len);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
@@ -90,6 +92,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 // 64 (bwd_dkdv64.hip); read rowstat.
 hipError_t launch_bwd_dkdv256(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv64(const BwdArgs& a, hipStream_t stream);
+
+// The short-document backward (bwd_short.hip): bf16, head_dim 64 or 128,
+// every segment at most kBinCap keys; dQ, dK and dV in one kernel over the
+// metadata's bins (no row statistics pass).
+bool bwd_short_applies(const BwdArgs& a);
+hipError_t launch_bwd_short(const BwdArgs& a, hipStream_t stream);
 
 // Fill n 16-bit words with zeros (a kernel, so it is safe under graph capture).
 hipError_t launch_zero_u16(void* p, int64_t n, hipStream_t stream);

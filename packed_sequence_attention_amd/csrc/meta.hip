@@ -236,6 +236,116 @@ __device__ void build_q_order(const int32_t* table, int n_seg, int batch, int se
   }
 }
 
+// The short-document bins (see kBinCap) of a table staged in LDS, built in
+// parallel by one workgroup of 256 threads.  The greedy walk in table order
+// (a document joins the open bin when it lies in the same batch row and the
+// bin's keys, with it, span at most kBinCap positions; otherwise it opens a
+// new bin) is a chain: from a bin's first segment s, the next bin starts at
+// next(s), the first later segment that lies in another batch row, is
+// padding, or ends more than kBinCap keys after s's first key (a binary
+// search: a row's documents are contiguous, so their key ends increase).
+// The bins start at the segments the chains from each row's first segment
+// reach; pointer doubling (log2 n rounds: reached nodes reach their 2^r-th
+// successor, and successors double) marks them, and a prefix count places
+// them in table order.  A segment of more than kBinCap keys, or more bins
+// than the bound, leaves the count at 0: no bins.
+struct BinLds {
+  int32_t jmp[2][kBinMaxSeg + 1];
+  uint8_t reach[kBinMaxSeg + 1];
+  int32_t wsum[4];
+  int flag;
+};
+
+__device__ void build_bins(const int32_t* table, int n_seg, int q_len, int64_t cap, int32_t* bins, BinLds& bl) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int32_t* cu_q = table;
+  const int32_t* cu_k = table + n_seg + 1;
+  const int32_t* kb = table + 2 * (n_seg + 1);
+  auto kn = [&](int s) { return cu_k[s + 1] - cu_k[s]; };
+  auto row = [&](int s) { return cu_q[s] / q_len; };
+  // 2 * (batch row) + (padding): within a batch row the documents come
+  // first, then at most one padding segment.
+  auto order_key = [&](int s) { return s >= n_seg ? INT_MAX : 2 * row(s) + (kn(s) == 0 ? 1 : 0); };
+  auto next_of = [&](int s) {
+    const int key = 2 * row(s);
+    int lo = s + 1, hi = n_seg;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (order_key(mid) > key) hi = mid; else lo = mid + 1;
+    }
+    const int stop = lo;
+    const int64_t lim = static_cast<int64_t>(kb[s]) + kBinCap;
+    lo = s + 1;
+    hi = stop;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (static_cast<int64_t>(kb[mid]) + kn(mid) > lim) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  };
+  if (tid == 0) bl.flag = 0;
+  __syncthreads();
+  for (int s = tid; s < n_seg; s += blockDim.x)
+    if (kn(s) > kBinCap) bl.flag = 1;
+  __syncthreads();
+  if (bl.flag != 0 || n_seg > kBinMaxSeg || q_len <= 0) {
+    if (tid == 0) bins[0] = 0;
+    return;
+  }
+  for (int s = tid; s <= n_seg; s += blockDim.x) {
+    int nx = n_seg;
+    bool head = false;
+    if (s < n_seg && kn(s) > 0) {
+      nx = next_of(s);
+      head = s == 0 || row(s - 1) != row(s);
+    }
+    bl.jmp[0][s] = nx;
+    bl.reach[s] = head ? 1 : 0;
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int r = 0; (1 << r) <= n_seg; ++r) {
+    for (int s = tid; s <= n_seg; s += blockDim.x) {
+      const int j = bl.jmp[cur][s];
+      if (bl.reach[s]) bl.reach[j] = 1;  // reached nodes only grow: a racing read is still a reached node
+      bl.jmp[cur ^ 1][s] = bl.jmp[cur][j];
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  // Bin starts: reached documents (padding and the sentinel are not bins).
+  // Each thread takes a contiguous run of segments; a workgroup scan of the
+  // runs' counts gives every start its bin index in table order.
+  const int per = (n_seg + static_cast<int>(blockDim.x) - 1) / static_cast<int>(blockDim.x);
+  const int s0 = min(n_seg, tid * per), s1 = min(n_seg, s0 + per);
+  int mine = 0;
+  for (int s = s0; s < s1; ++s) mine += bl.reach[s] && kn(s) > 0 ? 1 : 0;
+  int inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int x = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += x;
+  }
+  if (lane == 63) bl.wsum[wv] = inc;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x) / 64; ++w) {
+    before += w < wv ? bl.wsum[w] : 0;
+    total += bl.wsum[w];
+  }
+  int64_t idx = before + inc - mine;
+  for (int s = s0; s < s1; ++s) {
+    if (!(bl.reach[s] && kn(s) > 0)) continue;
+    if (idx < cap) {
+      bins[1 + 3 * idx] = cu_q[s];
+      bins[2 + 3 * idx] = cu_q[next_of(s)];
+      bins[3 + 3 * idx] = kb[s];
+    }
+    ++idx;
+  }
+  if (tid == 0) bins[0] = total <= cap ? total : 0;
+}
+
 // One launch for both halves: threads [0, n_rows) write row bounds, the
 // rest key bounds.  `block` is the workgroup's index among those doing this.
 __device__ __forceinline__ void meta_one(const int32_t* table, int n_seg, int seq_len, int row_offset,
@@ -252,36 +362,51 @@ __device__ __forceinline__ void meta_one(const int32_t* table, int n_seg, int se
   }
 }
 
-// With the query-tile order built (m.q_order non-null), workgroup 0 builds
-// it and the others (one more than the bounds need) write the bounds.
+// Workgroup roles of the metadata kernels: with the query-tile order built
+// (m.q_order non-null) workgroup 0 builds it; the next one builds the bins;
+// the others write the bounds.
 
-// Tables of up to this many segments are staged in LDS by the workgroup
-// that builds the query-tile order (its binary searches would otherwise wait
-// on global memory at every step); larger ones get no sorted order.
-constexpr int kOrderStageSeg = 2047;
+// Tables of up to this many segments are staged in LDS by the workgroups
+// that build the query-tile order and the bins (their binary searches and
+// walks would otherwise wait on global memory at every step); larger ones
+// get no sorted order.
+constexpr int kOrderStageSeg = kBinMaxSeg;
 
 __global__ void meta_kernel(const int32_t* __restrict__ table, int n_seg, int batch, int seq_len, int row_offset,
                             int q_len, int64_t n_rows, int64_t n_keys, MetaView m) {
-  __shared__ OrderLds ol;
+  __shared__ union {
+    OrderLds ol;
+    BinLds bl;
+  } u;
   __shared__ int32_t stage[3 * kOrderStageSeg + 2];
-  if (m.q_order != nullptr) {
-    if (blockIdx.x == 0) {
-      if (n_seg <= kOrderStageSeg) {
-        for (int i = threadIdx.x; i < 3 * n_seg + 2; i += blockDim.x) stage[i] = table[i];
-        __syncthreads();
-        build_q_order(stage, n_seg, batch, seq_len, row_offset, q_len, m, ol);
-      } else if (threadIdx.x == 0) {
-        // statistics that no kernel takes as a reason to follow the order
-        int32_t* st = const_cast<int32_t*>(m.q_stats);
-        st[0] = 0;
-        st[1] = 0x7FFFFFFF;
-      }
-      return;
+  const int ord = m.q_order != nullptr ? 1 : 0;
+  const int wg = static_cast<int>(blockIdx.x);
+  if (wg < ord + 1) {
+    const bool staged = n_seg <= kOrderStageSeg;
+    if (staged) {
+      for (int i = threadIdx.x; i < 3 * n_seg + 2; i += blockDim.x) stage[i] = table[i];
+      __syncthreads();
     }
-    meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, static_cast<int64_t>(blockIdx.x) - 1);
-  } else {
-    meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, blockIdx.x);
+    if (wg == ord) {
+      // (an empty chunk has no bin section; a table too long to stage gets no bins)
+      if (n_rows > 0) {
+        if (staged) {
+          build_bins(stage, n_seg, q_len, max_bins(batch, q_len), const_cast<int32_t*>(m.bins), u.bl);
+        } else if (threadIdx.x == 0) {
+          const_cast<int32_t*>(m.bins)[0] = 0;
+        }
+      }
+    } else if (staged) {
+      build_q_order(stage, n_seg, batch, seq_len, row_offset, q_len, m, u.ol);
+    } else if (threadIdx.x == 0) {
+      // statistics that no kernel takes as a reason to follow the order
+      int32_t* st = const_cast<int32_t*>(m.q_stats);
+      st[0] = 0;
+      st[1] = 0x7FFFFFFF;
+    }
+    return;
   }
+  meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, static_cast<int64_t>(wg) - ord - 1);
 }
 
 // The table passed by value in the kernel arguments (small tables): no
@@ -293,19 +418,24 @@ struct InlineTable {
 __global__ void meta_inline_kernel(InlineTable tab, int n_seg, int batch, int seq_len, int row_offset, int q_len,
                                    int64_t n_rows, int64_t n_keys, MetaView m) {
   __shared__ int32_t sh[kInlineTableInts];
-  __shared__ OrderLds ol;
+  __shared__ union {
+    OrderLds ol;
+    BinLds bl;
+  } u;
   const int n_int = 3 * n_seg + 2;
   for (int i = threadIdx.x; i < n_int; i += blockDim.x) sh[i] = tab.v[i];
   __syncthreads();
-  if (m.q_order != nullptr) {
-    if (blockIdx.x == 0) {
-      build_q_order(sh, n_seg, batch, seq_len, row_offset, q_len, m, ol);
-      return;
+  const int ord = m.q_order != nullptr ? 1 : 0;
+  const int wg = static_cast<int>(blockIdx.x);
+  if (wg < ord + 1) {
+    if (wg == ord) {
+      if (n_rows > 0) build_bins(sh, n_seg, q_len, max_bins(batch, q_len), const_cast<int32_t*>(m.bins), u.bl);
+    } else {
+      build_q_order(sh, n_seg, batch, seq_len, row_offset, q_len, m, u.ol);
     }
-    meta_one(sh, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, static_cast<int64_t>(blockIdx.x) - 1);
-  } else {
-    meta_one(sh, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, blockIdx.x);
+    return;
   }
+  meta_one(sh, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, static_cast<int64_t>(wg) - ord - 1);
 }
 
 }  // namespace
@@ -317,8 +447,8 @@ hipError_t launch_meta_build(const int32_t* table, bool host_table, int n_seg, i
   const int64_t n_keys = static_cast<int64_t>(batch) * seq_len;
   const int64_t n = n_rows + n_keys;
   if (n == 0) return hipSuccess;
-  // one more workgroup (the first) builds the query-tile order
-  dim3 grid(static_cast<unsigned>((n + 255) / 256 + (m.q_order != nullptr ? 1 : 0)));
+  // one more workgroup (the first) builds the query-tile order, one the bins
+  dim3 grid(static_cast<unsigned>((n + 255) / 256 + (m.q_order != nullptr ? 1 : 0) + 1));
   if (host_table) {
     InlineTable tab;
     const int n_int = 3 * n_seg + 2;
@@ -343,10 +473,11 @@ int device_cu_count() {
   return cached[dev];
 }
 
-size_t meta_order_ints(int batch, int seq_len, int q_len) {
+size_t meta_tail_ints(int batch, int seq_len, int q_len) {
   (void)seq_len;
-  // the order, then its two statistics, when an order is built
-  return order_built(batch, q_len) ? static_cast<size_t>(order_q_tiles(batch, q_len)) + 2 : 0;
+  // the order, then its two statistics, when an order is built; then the bins
+  return (order_built(batch, q_len) ? static_cast<size_t>(order_q_tiles(batch, q_len)) + 2 : 0) +
+         static_cast<size_t>(meta_bin_ints(batch, q_len));
 }
 
 }  // namespace bd

@@ -134,3 +134,53 @@ def per_doc_grad_errors(w, gpu, ref, heads=None, kv_heads=None):
                 if den > 0:
                     worst[name] = max(worst[name], float(np.linalg.norm(x - r) / den))
     return worst
+
+
+def tile_path(seg):
+    """Makes the backward of this segment table take the tile kernels (dQ
+    pass, then dK/dV pass) even when every segment is short: the descriptor
+    then says the longest segment is unknown.  Returns seg."""
+    seg.desc.max_seg_k = -1
+    return seg
+
+
+def greedy_bins(seg, cap=128):
+    """The short-document bins of a host segment table, walked in order
+    (documents of one batch row grouped while their keys span at most cap
+    positions; padding and a new batch row start a new bin): a list of
+    (first row, end row, first key) or None when a segment has more than cap
+    keys.  Written from the bins' definition in include/blockdiag.h."""
+    out, cur = [], None
+    for s in range(seg.n_seg):
+        q0, q1 = int(seg.cu_q[s]), int(seg.cu_q[s + 1])
+        kn = int(seg.cu_k[s + 1] - seg.cu_k[s])
+        k0 = int(seg.k_begin[s])
+        if kn == 0:
+            if cur is not None:
+                out.append(tuple(cur))
+            cur = None
+            continue
+        if kn > cap:
+            return None
+        if cur is not None and q0 // seg.q_len == cur[0] // seg.q_len and k0 + kn - cur[2] <= cap:
+            cur[1] = q1
+            continue
+        if cur is not None:
+            out.append(tuple(cur))
+        cur = [q0, q1, k0]
+    if cur is not None:
+        out.append(tuple(cur))
+    return out
+
+
+def device_bins(seg):
+    """The bins the metadata build wrote (the section after the bounds and
+    the query-tile order), as a list of (first row, end row, first key)."""
+    m = seg.meta.cpu().numpy()
+    B, S, L = seg.batch, seg.seq_len, seg.q_len
+    off = 2 * B * L + 2 * B * S
+    nq = B * ((L + 31) // 32)
+    if 1 <= nq <= 8192:
+        off += nq + 2
+    n = int(m[off])
+    return [tuple(int(x) for x in m[off + 1 + 3 * i: off + 4 + 3 * i]) for i in range(n)]

@@ -180,8 +180,11 @@ def test_attention_entry_points_reject_before_launch():
     # ... a metadata buffer smaller than blockdiag_meta_ints, and a missing descriptor
     assert lib.blockdiag_meta_build(p, None, 1, 1, 64, 0, 64, p, cap - 1, ctypes.byref(desc), N) == 3
     assert lib.blockdiag_meta_build(p, None, 1, 1, 64, 0, 64, p, cap, None, N) == 1
-    # bounds of rows and keys, then the order of the 32-row query tiles and its two statistics
-    assert lib.blockdiag_meta_ints(2, 100, 40) == 2 * 2 * 40 + 2 * 2 * 100 + 2 * 2 + 2
+    # bounds of rows and keys, the order of the 32-row query tiles and its two
+    # statistics, then the bins: a count and 3 per bin, at most
+    # batch * (2 * ceil((q_len + 127) / 128) + 1) of them
+    assert lib.blockdiag_meta_ints(2, 100, 40) == 2 * 2 * 40 + 2 * 2 * 100 + 2 * 2 + 2 + 1 + 3 * 2 * (2 * 2 + 1)
+    assert lib.blockdiag_meta_ints(1, 1000, 1000) == 2 * 1000 + 2 * 1000 + 32 + 2 + 1 + 3 * (2 * 9 + 1)
 
 
 def test_meta_build_host_rejects_before_launch():

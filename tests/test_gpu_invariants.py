@@ -4,9 +4,12 @@
   distributed): block-diagonal varlen CP for packed sequences"): O and LSE of
   contiguous chunks concatenated equal the single full call bit for bit
   (key tiles are anchored at fixed positions of the row, so a row's
-  arithmetic does not depend on the chunk), and so does dQ (its rows are
-  computed independently, over the same key tiles); dK/dV sum over chunks to
-  the full call's within tolerance;
+  arithmetic does not depend on the chunk), and so does dQ from the tile
+  kernels (its rows are computed independently, over the same key tiles;
+  these tests keep every call on the tile kernels, since a chunk of only
+  short documents would otherwise take the short-document kernel, which sums
+  in another order); dK/dV sum over chunks to the full call's within
+  tolerance;
 * forward and backward are bitwise deterministic (a replayed forward under
   activation checkpointing equals the original, Design overview, packed.py);
 * documents are independent: changing one document's inputs leaves every
@@ -45,14 +48,14 @@ def test_chunk_concatenation(cp):
     S = 2048
     w, t = H.small_case(200 + cp, "bf16", docs, S, 0, S, 32, 8, 128)
     d = H.to_device(w, t)
-    full = bd.segment(docs, S, 0, S, device="cuda")
+    full = H.tile_path(bd.segment(docs, S, 0, S, device="cuda"))
     o, lse = bd.attn_fwd(d["q"], d["k"], d["v"], full)
     dq, dk, dv = bd.attn_bwd(d["q"], d["k"], d["v"], o, lse, d["do"], full)
     dk_sum = torch.zeros_like(dk, dtype=torch.float32)
     dv_sum = torch.zeros_like(dv, dtype=torch.float32)
     bounds = np.linspace(0, S, cp + 1).astype(int)
     for a, b in zip(bounds[:-1], bounds[1:]):
-        seg = bd.segment(docs, S, int(a), int(b - a), device="cuda")
+        seg = H.tile_path(bd.segment(docs, S, int(a), int(b - a), device="cuda"))
         qc = d["q"][:, a:b].contiguous(); doc_ = d["do"][:, a:b].contiguous()
         oc, lc = bd.attn_fwd(qc, d["k"], d["v"], seg)
         assert torch.equal(oc, o[:, a:b]), "O differs from the full call"
@@ -273,13 +276,13 @@ def test_chunk_concatenation_any_gqa_ratio(hq, hkv, d):
     S, cp = 2048, 4
     w, t = H.small_case(250 + hq + d, "bf16", docs, S, 0, S, hq, hkv, d)
     dd = H.to_device(w, t)
-    full = bd.segment(docs, S, 0, S, device="cuda")
+    full = H.tile_path(bd.segment(docs, S, 0, S, device="cuda"))
     o, lse = bd.attn_fwd(dd["q"], dd["k"], dd["v"], full)
     dq, dk, dv = bd.attn_bwd(dd["q"], dd["k"], dd["v"], o, lse, dd["do"], full)
     dk_sum = torch.zeros_like(dk, dtype=torch.float32)
     bounds = [0, 500, 1100, 1600, 2048]   # uneven chunks, not multiples of 32
     for a, b in zip(bounds[:-1], bounds[1:]):
-        seg = bd.segment(docs, S, a, b - a, device="cuda")
+        seg = H.tile_path(bd.segment(docs, S, a, b - a, device="cuda"))
         qc, doc_ = dd["q"][:, a:b].contiguous(), dd["do"][:, a:b].contiguous()
         oc, lc = bd.attn_fwd(qc, dd["k"], dd["v"], seg)
         assert torch.equal(oc, o[:, a:b]) and torch.equal(lc, lse[:, :, a:b])
