@@ -17,31 +17,27 @@
 // kernels (a dQ pass and a dK/dV pass, each recomputing S and dP and
 // reading Q and dO) move about 1.6 times the bytes.
 //
-// Work decomposition: eight waves in two groups of four; the bin's K and V
-// rows sit in LDS.  The bin's iterations are its 32-row blocks times the
-// GQA group's query heads (rows outer, heads inner: the heads of a row are
-// adjacent in memory); the two groups take alternate iterations, each with
-// its own double buffer, so two blocks are in flight, and one group runs a
-// barrier behind the other (ping-pong), so their key phases (matrix cores,
-// exponentials) and their light phases overlap.  Wave w of a group
+// Work decomposition: four waves, two workgroups per CU.  The bin's
+// iterations are its 32-row blocks times the GQA group's query heads (rows
+// outer, heads inner: the heads of a row are adjacent in memory).  Wave w
 // owns key block w of the bin (keys 32w .. 32w + 31 from the bin's first
-// key; dK and dV accumulated in registers over the group's iterations, the
-// two groups' partial sums added at the end in a fixed order) and, in the
-// dQ products, columns 32w .. 32w + 31 of head_dim.
+// key: K rows in LDS, V fragments in registers, dK and dV accumulated in
+// registers over the whole bin) and, in the dQ products, columns 32w ..
+// 32w + 31 of head_dim.
 // Per iteration (row block, head), v_mfma_f32_32x32x16_bf16 throughout:
 //   stats  delta of the block's rows from O (registers) and dO (LDS),
 //          with lse * log2(e), into LDS;
 //   keys   wave w, if a row of the block attends a key of its block:
-//          S = Q K^T, dP = dO V^T (A = Q / dO rows, B = K / V rows, LDS),
+//          S = Q K^T, dP = dO V^T (A = Q / dO rows from LDS, B = K rows
+//          from LDS / V in registers),
 //          P and dS in the accumulator layout (lane: key), then
 //          dV^T += dO^T P and dK^T += Q^T dS (A = dO^T / Q^T with the LDS
 //          transpose load); dS in bf16 goes to LDS, key-major;
 //   dQ     wave w: dQ^T[32w .. 32w + 31] = sum over the live key blocks of
 //          K^T dS^T (A = K^T, B = dS^T, both with the transpose load),
 //          written once for the block's rows that are the bin's.
-// Q / dO blocks come in by direct global -> LDS loads into each group's
-// double buffer, one block of the group ahead; O rows for delta likewise,
-// in registers.
+// Q / dO blocks come in by direct global -> LDS loads into a double
+// buffer, one block ahead; O rows for delta likewise, in registers.
 // Rows and keys past the bin inside a 32-row or 32-key block are another
 // bin's: a key's row interval from the metadata masks them, and nothing of
 // theirs is written.  Rows of padding and keys no row attends lie in no
@@ -58,11 +54,10 @@ namespace bd {
 namespace {
 
 constexpr int kSB = 32;  // rows / keys of a block
-constexpr int kSW = 4;   // waves per group = key blocks of a bin
-static_assert(kSB * kSW == kBinCap, "a group's key blocks cover a bin");
+constexpr int kSW = 4;   // waves = key blocks of a bin
+static_assert(kSB * kSW == kBinCap, "the waves' key blocks cover a bin");
 constexpr int kZT = 64;          // rows / keys of a zero-fill tile
-constexpr int kThreads = 512;    // two groups of four waves
-constexpr int kGroupThreads = 256;
+constexpr int kThreads = 256;  // four waves; two workgroups per CU (LDS and registers)
 
 template <int D>
 struct ShortLds {
@@ -71,10 +66,10 @@ struct ShortLds {
   static constexpr int ktile = kBinCap * RP;      // the bin's K (or V) rows
   static constexpr int qtile = kSB * RP;          // one 32-row block of Q or dO
   static constexpr int stage = 2 * qtile;         // Q then dO
-  static constexpr int PER_T = kSB * CH / kGroupThreads;  // direct loads per thread of a group per tensor
+  static constexpr int PER_T = kSB * CH / kThreads;  // direct loads per thread per tensor
   static constexpr int DSP = kSB * 2 + 8;         // dS tile pitch: a key's 32 rows + 8 bytes
   static constexpr int dstile = kSB * DSP;        // one key block's dS (key-major)
-  static_assert(PER_T * kGroupThreads == kSB * CH, "whole tensors per load round");
+  static_assert(PER_T * kThreads == kSB * CH, "whole tensors per load round");
 };
 
 // Chunk swizzle of row r: 16 rows of a row read, and 4 rows x 4 chunks of a
@@ -160,7 +155,7 @@ __device__ void zero_tile(const AttnShape& s, const MetaView& m, uint16_t* dq, u
 }
 
 template <int D, bool DROP>
-__global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
+__global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ d_o, const uint16_t* __restrict__ o, const float* __restrict__ lse, MetaView m,
     uint16_t* __restrict__ dq, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int n_bin_wg, int n_zr) {
@@ -169,16 +164,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
   constexpr int OE = D / 64;  // 16-byte chunks of O per lane in the delta step
   using L = ShortLds<D>;
   constexpr int RP = L::RP;
-  // Separate LDS objects for the stages of each group, so the compiler
-  // knows that direct loads into one do not alias reads of another.
-  __shared__ __attribute__((aligned(16))) char stA0[L::stage];
-  __shared__ __attribute__((aligned(16))) char stA1[L::stage];
-  __shared__ __attribute__((aligned(16))) char stB0[L::stage];
-  __shared__ __attribute__((aligned(16))) char stB1[L::stage];
+  // The two stages are separate LDS objects, so the compiler knows that
+  // direct loads into one do not alias reads of the other.
+  __shared__ __attribute__((aligned(16))) char st0[L::stage];
+  __shared__ __attribute__((aligned(16))) char st1[L::stage];
   __shared__ __attribute__((aligned(16))) char sK[L::ktile];
-  __shared__ __attribute__((aligned(16))) char sV[L::ktile];
-  __shared__ __attribute__((aligned(16))) char sdS[2][kSW * L::dstile];
-  __shared__ __attribute__((aligned(16))) float2 sStat[2][kSB];  // (lse * log2(e), delta) per block row
+  __shared__ __attribute__((aligned(16))) char sdS[kSW * L::dstile];
+  __shared__ __attribute__((aligned(16))) float2 sStat[kSB];  // (lse * log2(e), delta) per block row
   __shared__ int sRng[2][kSW];                                   // local rows attending each key block
   typedef __attribute__((address_space(3))) void lds_void;
 
@@ -206,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wk = wave & 3;  // head group; key block (and dQ column block)
+  const int wk = wave;  // key block (and dQ column block)
   const int G = s.group;
   const int row_stride = s.h_q * D;
 
@@ -217,19 +209,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
   const int64_t kv_row_c =
       (static_cast<int64_t>(b) * s.kv_len + ((kok ? kpos : pos0) - s.kv_begin)) * s.h_kv + g;
 
-  // Iteration it of the bin: row block it / G, head g * G + it % G.  Group
-  // grp takes iterations 2 j + grp, j = 0 .. n_js - 1 (the second group's
-  // last one may be past the end: it then only keeps the barriers).
+  // Iteration it of the bin: row block it / G, head g * G + it % G.
   const int n_rb = (nrows + kSB - 1) / kSB;
   const int n_it = n_rb * G;
-  const int n_js = (n_it + 1) / 2;
 
-  // Direct loads of the Q / dO block of iteration it into stage buf of this
-  // group: chunk ci = i * 256 + (thread index in the group) of each tensor
-  // lands at LDS chunk ci, so each lane fetches the global chunk that
-  // belongs there under the swizzle.  Rows past the chunk read as zero.
+  // Direct loads of the Q / dO block of iteration it into stage buf: chunk
+  // ci = i * 256 + tid of each tensor lands at LDS chunk ci, so each lane
+  // fetches the global chunk that belongs there under the swizzle.  Rows
+  // past the chunk read as zero.
   auto issue_tile = [&](int it, int buf) __attribute__((always_inline)) {
-    char* dst = grp == 0 ? (buf == 0 ? stA0 : stA1) : (buf == 0 ? stB0 : stB1);
+    char* dst = buf == 0 ? st0 : st1;
     const int ib = it / G, h = g * G + it % G;
     const int trow0 = t0 + ib * kSB;
     const int64_t tile0 = ((static_cast<int64_t>(b) * s.q_len + trow0) * s.h_q + h) * D;
@@ -242,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
           const_cast<uint16_t*>((tensor == 0 ? q : d_o) + tile0), 0, nbytes, 0x00020000);
 #pragma unroll
       for (int i = 0; i < L::PER_T; ++i) {
-        const int cw = i * kGroupThreads + wk * 64;  // the wave's first chunk of the tensor (uniform)
+        const int cw = i * kThreads + wk * 64;  // the wave's first chunk of the tensor (uniform)
         const int lc = cw + lane;
         const int r = lc / L::CH, pc = (lc % L::CH) ^ swz<D>(r);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + tensor * L::qtile + cw * 16), 16,
@@ -265,26 +254,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
     lsev = lse[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t];
   };
 
-  if (grp < n_it) {
-    issue_tile(grp, 0);
-    load_o(grp);
-  }
-  // K (group 0) or V (group 1) rows of this wave's key block into LDS, in
-  // the swizzled layout; keys past the bin are zero.
+  issue_tile(0, 0);  // (n_it >= 1: a bin has a row)
+  load_o(0);
+  // K rows of this wave's key block into LDS (swizzled) and V fragments
+  // (B operand of dP) in registers; keys past the bin are zero.
+  bf16x8 vf[KK];
   {
     const int kg = lane >> 5;
-    const uint16_t* src = (grp == 0 ? k : v) + kv_row_c * D + kg * 8;
-    char* dst = grp == 0 ? sK : sV;
     bf16x8 x[KK];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) x[kk] = *reinterpret_cast<const bf16x8*>(src + kk * 16);
+    for (int kk = 0; kk < KK; ++kk) {
+      x[kk] = *reinterpret_cast<const bf16x8*>(k + kv_row_c * D + kg * 8 + kk * 16);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(v + kv_row_c * D + kg * 8 + kk * 16);
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       if (!kok) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[kk][i] = static_cast<__bf16>(0.f);
+        for (int i = 0; i < 8; ++i) x[kk][i] = vf[kk][i] = static_cast<__bf16>(0.f);
       }
-      *reinterpret_cast<bf16x8*>(dst + kb0 * RP + (((2 * kk + kg) ^ swz<D>(kb0)) << 4)) = x[kk];
+      *reinterpret_cast<bf16x8*>(sK + kb0 * RP + (((2 * kk + kg) ^ swz<D>(kb0)) << 4)) = x[kk];
     }
   }
   int a0 = 0, a1 = 0;
@@ -299,12 +288,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
   const int mask_lo = att ? a0 : 0;
   const unsigned mask_span = att ? static_cast<unsigned>(a1 - a0) : 0u;
   const int wqlo = wave_min_i(att ? a0 : INT_MAX), wqhi = wave_max_i(att ? a1 : INT_MIN);
-  if (lane == 0 && grp == 0) {
+  if (lane == 0) {
     sRng[0][wk] = wqlo;
     sRng[1][wk] = wqhi;
   }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // K and V rows, the key blocks' row ranges and each group's first block in LDS
+  __syncthreads();  // K rows, the key blocks' row ranges and the first block in LDS
   int rlo[kSW], rhi[kSW];
 #pragma unroll
   for (int j = 0; j < kSW; ++j) {
@@ -319,13 +308,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
     for (int j = 0; j < 16; ++j) dkacc[db][j] = dvacc[db][j] = 0.f;
 
   const float c = s.scale * kLog2e;
-  char* sdSg = sdS[grp];
-  float2* sSt = sStat[grp];
+  char* sdSg = sdS;
+  float2* sSt = sStat;
 
-  // A block's dQ rows are stored at the start of the group's next
-  // iteration (or after the last one), not before the wait at the end of
-  // their own: vmcnt counts stores too, and that wait is for the next
-  // blocks' loads only.
+  // A block's dQ rows are stored at the start of the next iteration (or
+  // after the last one), not before the wait at the end of their own: vmcnt
+  // counts stores too, and that wait is for the next block's loads only.
   uint2 pend[4];
   uint16_t* pend_out = nullptr;
   auto store_pending = [&]() __attribute__((always_inline)) {
@@ -336,17 +324,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
     pend_out = nullptr;
   };
 
-  auto step = [&](int j, auto stage) __attribute__((always_inline)) {
+  auto step = [&](int it, auto stage) __attribute__((always_inline)) {
     constexpr int buf = decltype(stage)::value;
-    const int it = 2 * j + grp;
-    const bool valid = it < n_it;
     const int ib = it / G, h = g * G + it % G;
     const int trow0 = t0 + ib * kSB;  // the block's first local row
-    const char* sQ = grp == 0 ? (buf == 0 ? stA0 : stA1) : (buf == 0 ? stB0 : stB1);
+    const char* sQ = buf == 0 ? st0 : st1;
     const char* sdO = sQ + L::qtile;
-    // The group's next block goes to the other stage (last read before
-    // the last barrier).
-    if (it + 2 < n_it) issue_tile(it + 2, buf ^ 1);
+    // The next block goes to the other stage (last read before the last
+    // barrier).
+    if (it + 1 < n_it) issue_tile(it + 1, buf ^ 1);
     store_pending();
     // Per-lane LDS offsets from an opaque copy of the lane index: hoisted
     // out of the loop, they would hold registers that the dK / dV
@@ -362,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
 
     // Row statistics of the block: delta = dO . O (float32) over 8 lanes
     // per row, and lse in base 2.  Rows past the chunk take zeros.
-    if (valid) {
+    {
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < OE; ++e) {
@@ -376,11 +362,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
       const bool in_chunk = trow0 + drow < s.q_len;
       if (dc == 0) sSt[drow] = in_chunk ? make_float2(lsev * kLog2e, part) : make_float2(0.f, 0.f);
     }
-    if (it + 2 < n_it) load_o(it + 2);
+    if (it + 1 < n_it) load_o(it + 1);
     lds_barrier();  // statistics of the block
 
     // Key phase: S, dP, softmax and dS for this wave's key block; dV, dK.
-    const bool live = valid && wqlo < trow0 + kSB && wqhi > trow0;
+    const bool live = wqlo < trow0 + kSB && wqhi > trow0;
     if (live) {
       f32x16 sacc, pacc;
 #pragma unroll
@@ -392,9 +378,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + pos);
         const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sdO + pos);
         const bf16x8 bk = *reinterpret_cast<const bf16x8*>(sK + kpos_l);
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sV + kpos_l);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
-        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, pacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], pacc, 0, 0, 0);
         // LDS reads at most two k-steps ahead of their products
         if (kk % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
@@ -458,8 +443,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
     }
     lds_barrier();  // dS of every live key block
 
-    // dQ phase: wave wk < DB of the group owns columns 32 wk .. 32 wk + 31.
-    if (valid && wk < DB) {
+    // dQ phase: wave wk < DB owns columns 32 wk .. 32 wk + 31.
+    if (wk < DB) {
       f32x16 qacc;
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) qacc[jj] = 0.f;
@@ -481,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
         }
       }
       // qacc[jj] = dQ^T[d = 32 wk + (jj/4)*8 + kg*4 + jj%4][row trow0 + n];
-      // stored at the start of the group's next iteration
+      // stored at the start of the next iteration
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         pend[jq].x = pack_bf16x2(qacc[4 * jq] * s.scale, qacc[4 * jq + 1] * s.scale);
@@ -494,52 +479,30 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_short_kernel(
     __builtin_amdgcn_s_waitcnt(0);  // the next blocks' direct loads and O rows have landed
     __syncthreads();                // next stages ready; dS and statistics free
   };
-  // Ping-pong: group 1 runs one barrier behind group 0, so the two groups'
-  // key phases (matrix cores, exponentials) fall between different barriers.
-  if (grp == 1) lds_barrier();
-  for (int j = 0; j < n_js; j += 2) {
-    step(j, Stage<0>{});
-    if (j + 1 < n_js) step(j + 1, Stage<1>{});
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, Stage<0>{});
+    if (it + 1 < n_it) step(it + 1, Stage<1>{});
   }
-  if (grp == 0) lds_barrier();
   store_pending();
 
-  // The two groups' partial dK and dV of each key block, added in a fixed
-  // order (group 0 + group 1) through LDS (K and V are no longer read):
-  // wave wk of group 1 stores its partial (lane-major float4) into half of
-  // sK or sV, wave wk of group 0 adds it and writes the sum.
   // dkacc[db][jj] = dK^T[d = 32db + (jj/4)*8 + kg*4 + jj%4][key kb0]
-  constexpr int PART4 = DB * 4 * 64;  // float4 per partial
-  static_assert(2 * PART4 * 16 <= L::ktile, "two partials fit in sK, two in sV");
-  float4* part = reinterpret_cast<float4*>(wk < 2 ? sK : sV) + (wk & 1) * PART4;
-  const int64_t kv_row = (static_cast<int64_t>(b) * s.kv_len + (kpos - s.kv_begin)) * s.h_kv + g;
-  auto reduce = [&](f32x16 (&acc)[DB], uint16_t* out, float mul) __attribute__((always_inline)) {
-    if (grp == 1) {
+  if (kok) {
+    const int64_t kv_row = (static_cast<int64_t>(b) * s.kv_len + (kpos - s.kv_begin)) * s.h_kv + g;
+    uint16_t* dkr = dk + kv_row * D + (lane >> 5) * 4;
+    uint16_t* dvr = dv + kv_row * D + (lane >> 5) * 4;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int jq = 0; jq < 4; ++jq)
-          part[(db * 4 + jq) * 64 + lane] =
-              make_float4(acc[db][4 * jq], acc[db][4 * jq + 1], acc[db][4 * jq + 2], acc[db][4 * jq + 3]);
-    }
-    __syncthreads();
-    if (grp == 0 && kok) {
-      uint16_t* row = out + kv_row * D + (lane >> 5) * 4;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const float4 x = part[(db * 4 + jq) * 64 + lane];
-          uint2 pk;
-          pk.x = pack_bf16x2((acc[db][4 * jq] + x.x) * mul, (acc[db][4 * jq + 1] + x.y) * mul);
-          pk.y = pack_bf16x2((acc[db][4 * jq + 2] + x.z) * mul, (acc[db][4 * jq + 3] + x.w) * mul);
-          *reinterpret_cast<uint2*>(row + db * 32 + jq * 8) = pk;
-        }
-    }
-    __syncthreads();
-  };
-  reduce(dkacc, dk, s.scale);
-  reduce(dvacc, dv, 1.f);
+      for (int jq = 0; jq < 4; ++jq) {
+        uint2 a2, bb;
+        a2.x = pack_bf16x2(dkacc[db][4 * jq] * s.scale, dkacc[db][4 * jq + 1] * s.scale);
+        a2.y = pack_bf16x2(dkacc[db][4 * jq + 2] * s.scale, dkacc[db][4 * jq + 3] * s.scale);
+        bb.x = pack_bf16x2(dvacc[db][4 * jq], dvacc[db][4 * jq + 1]);
+        bb.y = pack_bf16x2(dvacc[db][4 * jq + 2], dvacc[db][4 * jq + 3]);
+        *reinterpret_cast<uint2*>(dkr + db * 32 + jq * 8) = a2;
+        *reinterpret_cast<uint2*>(dvr + db * 32 + jq * 8) = bb;
+      }
+  }
 }
 
 template <int D, bool DROP>
