@@ -92,6 +92,13 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, ab);
 }
 
+// A lane's value moved by a DPP pattern (quad permutation 0x00-0xFF, 0x141
+// mirror within each group of 8 lanes); all lanes take part.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 // Workgroup barrier for LDS data written by the waves: waits for this
 // wave's LDS operations only, not for direct global -> LDS loads in flight
 // (a fence on the workgroup would wait for those too).
@@ -356,9 +363,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) part = fmaf(static_cast<float>(x[i]), static_cast<float>(ov[e][i]), part);
       }
-      part += __shfl_xor(part, 1, 64);
-      part += __shfl_xor(part, 2, 64);
-      part += __shfl_xor(part, 4, 64);
+      // sum over the row's 8 lanes with DPP moves (lane ^ 1, lane ^ 2 in
+      // a quad, then lane 7 - i in a group of 8): no LDS round trips
+      part += dpp_move<0xB1>(part);
+      part += dpp_move<0x4E>(part);
+      part += dpp_move<0x141>(part);
       const bool in_chunk = trow0 + drow < s.q_len;
       if (dc == 0) sSt[drow] = in_chunk ? make_float2(lsev * kLog2e, part) : make_float2(0.f, 0.f);
     }
