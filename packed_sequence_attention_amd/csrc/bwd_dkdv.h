@@ -149,11 +149,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   typedef __attribute__((address_space(3))) void lds_void;
   // Per-lane part of the direct-load offsets: load i of a wave covers RPL
   // tile rows (64 lanes x 16 bytes = 4 rows of 16 chunks for head_dim 128,
-  // 8 rows of 8 for 64).  The swizzle of row r depends on r % 16 only, so
-  // the lane's offset repeats every PER loads plus 16 rows; the row part
-  // common to the wave goes into the resource base.
+  // 8 rows of 8 for 64); the row part common to the wave goes into the
+  // resource base.
   constexpr int RPL = 64 / CH;  // rows per direct load
-  constexpr int PER = 16 / RPL;
   // With live == false (a padding iteration) the loads read nothing and
   // write zeros; tiles starting past the chunk read zeros as well.
   auto issue_tile = [&](int h, int t0, int buf, bool live) {
@@ -167,18 +165,19 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     char* dst = hb + kgrp * (kQB * L::QP);
     // Recomputed here rather than kept live across the loop: the opaque copy
     // of the lane index stops the compiler from hoisting (and then spilling)
-    // these offsets, whose reload would wait on the direct loads in flight.
+    // this offset, whose reload would wait on the direct loads in flight.
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    int lane_off[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int r = i * RPL + ln / CH;  // tile row of load i (mod 16 rows)
-      lane_off[i] = (r * row_stride + ((ln % CH) ^ qswz<D>(r)) * 8) * 2;
-    }
+    // Load i covers tile rows i * RPL + ln / CH.  The swizzle splits over
+    // the two parts of the row index, qswz(i * RPL + x) = qswz(i * RPL) ^
+    // qswz(x) (x < RPL), and the row pitch in bytes is a multiple of 16
+    // chunks, so load i's offset is the lane's offset for load 0 with the
+    // chunk bits xor-ed by qswz(i * RPL), plus i * RPL rows: one xor-add.
+    const int row_bytes = row_stride * 2;
+    const int off0 = (ln / CH) * row_bytes + (((ln % CH) ^ qswz<D>(ln / CH)) << 4);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int voff = lane_off[i % PER] + (i / PER) * 16 * row_stride * 2;
+      const int voff = (off0 ^ (qswz<D>((i * RPL) & 15) << 4)) + i * RPL * row_bytes;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + i * 64 * 16), 16, voff, 0, 0, 0);
     }
     if (kgrp == 1) {  // the tile's (lse * log2(e), delta) pairs: 64 x 4 bytes
@@ -350,6 +349,15 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     // branch).
     auto finish = [&](auto masked) {
       float pv[16], dsv[16];
+      // The key's allowed rows [mask_lo, mask_lo + mask_span) as bits of
+      // row - (t0 + kg*4), clamped to the 32 bits.
+      uint32_t allow = 0;
+      if constexpr (decltype(masked)::value) {
+        const int rb = t0 + kg * 4;
+        const int a = min(max(mask_lo - rb, 0), 32);
+        const int e = min(max(mask_lo + static_cast<int>(mask_span) - rb, 0), 32);
+        allow = (a >= 32 ? 0u : ~0u << a) & (e >= 32 ? ~0u : (1u << e) - 1u);
+      }
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
         const int r0 = jq * 8 + kg * 4;
@@ -366,11 +374,15 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = jq * 4 + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -lsv[e]));
+          float x = fmaf(sacc[j], c, -lsv[e]);
           if constexpr (decltype(masked)::value) {
-            const unsigned rel = static_cast<unsigned>(t0 + r0 + e - mask_lo);
-            p = rel < mask_span ? p : 0.f;  // a select: also clears inf on padding rows
+            // bit (j/4)*8 + j%4 of allow: row t0 + kg*4 + that is allowed;
+            // elsewhere the exponent becomes -inf, so P = 0 (also on padding
+            // rows, whose exponent may be +inf)
+            const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(allow), jq * 8 + e, 1));
+            x = __uint_as_float((__float_as_uint(x) & keep) | (0xff800000u & ~keep));
           }
+          const float p = __builtin_amdgcn_exp2f(x);
           pv[j] = DROP ? p * zf[e] : p;
           dsv[j] = DROP ? p * (pacc[j] * zf[e] - dev[e]) : p * (pacc[j] - dev[e]);
         }

@@ -309,10 +309,16 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
         // P = 0): a test inside the exp loop would be split into one branch
         // per element and keep the exps from overlapping the products.
         if (!full) {
+          // The row's allowed keys [lo, hi) as bits of key - kb (bit pos of
+          // element j: (j/4)*8 + j%4); element j keeps its score where its
+          // bit is set and becomes -inf elsewhere (two instructions each).
+          const int kb = k0 + sb * 32 + kg * 4;
+          const int a = min(max(lo - kb, 0), 32), e = min(max(hi - kb, 0), 32);
+          const uint32_t allow = (a >= 32 ? 0u : ~0u << a) & (e >= 32 ? ~0u : (1u << e) - 1u);
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int key = k0 + sb * 32 + (j >> 2) * 8 + kg * 4 + (j & 3);
-            if (key < lo || key >= hi) sacc[j] = -INFINITY;
+            const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(allow), (j >> 2) * 8 + (j & 3), 1));
+            sacc[j] = __uint_as_float((__float_as_uint(sacc[j]) & keep) | (0xff800000u & ~keep));
           }
         }
         // K^T transpose reads of the dQ^T products, flattened over (k-step,

@@ -289,10 +289,16 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
         }
         // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
         if (!full) {
+          // The row's allowed keys [lo, hi) as bits of key - kb (bit pos of
+          // element j: (j/4)*8 + j%4); element j keeps its score where its
+          // bit is set and becomes -inf elsewhere (two instructions each).
+          const int kb = k0 + sb * 32 + kg * 4;
+          const int a = min(max(lo - kb, 0), 32), e = min(max(hi - kb, 0), 32);
+          const uint32_t allow = (a >= 32 ? 0u : ~0u << a) & (e >= 32 ? ~0u : (1u << e) - 1u);
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
-            const int key = k0 + sb * 32 + (j >> 2) * 8 + kg * 4 + (j & 3);
-            if (key < lo || key >= hi) sacc[j] = -INFINITY;
+            const uint32_t keep = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(allow), (j >> 2) * 8 + (j & 3), 1));
+            sacc[j] = __uint_as_float((__float_as_uint(sacc[j]) & keep) | (0xff800000u & ~keep));
           }
         }
         // V^T transpose reads of the O^T products, flattened over (k-step,
@@ -311,30 +317,39 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
           for (int st_ = 0; st_ < PFV; ++st_) vq[st_] = vread(st_);
           __builtin_amdgcn_sched_barrier(0);
         }
+        // (maximum: no NaN quieting of the operands, three per instruction)
         float mx = sacc[0];
 #pragma unroll
-        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sacc[j]);
+        for (int j = 1; j < 16; ++j) mx = __builtin_elementwise_maximum(mx, sacc[j]);
         mx = pair32_max(mx);
-        const float mnew = fmaxf(mrun, mx * c);
+        const float mnew = __builtin_elementwise_maximum(mrun, mx * c);
         const bool need = mnew > mrun + 8.f;
-        if (__any(need)) {
-          const float alpha = need ? exp2f(mrun - mnew) : 1.f;
-          if (need) mrun = mnew;
+        // A row whose reference is still -inf has accumulated nothing (every
+        // weight so far was exp2(-inf) = 0): it takes the new reference
+        // without a rescale, so the first live tile of a row costs none.
+        const bool resc = need && mrun != -INFINITY;
+        if (__any(resc)) {
+          const float alpha = resc ? __builtin_amdgcn_exp2f(mrun - mnew) : 1.f;
           lrun *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int j = 0; j < 16; ++j) oacc[db][j] *= alpha;
         }
+        if (need) mrun = mnew;
         const float mu = (mrun == -INFINITY) ? 0.f : mrun;
         float p[16];
-        float ps = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -mu));
-          ps += p[j];
-        }
-        lrun += ps;
+        for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(sacc[j], c, -mu));
+        // The row sum in float32 (of the undropped weights), as a tree.
+        float ps[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ps[j] = p[j] + p[8 + j];
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+          for (int j = 0; j < w; ++j) ps[j] += ps[j + w];
+        lrun += ps[0];
         if constexpr (DROP) {
           // dropout of the weights that multiply V (the row sum above is the
           // undropped one): this lane's row, keys in groups of 4
