@@ -154,6 +154,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   constexpr int RPL = 64 / CH;  // rows per direct load
   // With live == false (a padding iteration) the loads read nothing and
   // write zeros; tiles starting past the chunk read zeros as well.
+  // (The prologue's loads; the loop issues its own, spread over the S / dP
+  // products.  Keeping the buffer resources in a struct or returning them
+  // from a lambda made the host pass drop a kernel's launch stub, so the
+  // loop's copy of this code uses plain locals.)
   auto issue_tile = [&](int h, int t0, int buf, bool live) {
     // row t0 of (b, h); bytes from there to the end of the tensor's rows for this head
     const int64_t tile0 = ((static_cast<int64_t>(b) * s.q_len + t0) * s.h_q + h) * D;
@@ -288,8 +292,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // group B (heads 2, 3) each put one wave on every SIMD, and while one
   // group runs the softmax (vector ALU) the other keeps the matrix cores
   // busy with S and dP.  Per wave, iteration it is
-  //   H1: direct loads of tile it+1 into the other stage; S and dP products
-  //   (barrier: scheduling only, no memory ordering)
+  //   H1: S and dP products, with the direct loads of tile it+1 into the
+  //   other stage between them (barrier: scheduling only, no memory ordering)
   //   H2: softmax, dV/dK products of tile it; wait for the direct loads;
   //   barrier.
   // Group B enters the loop one barrier later and group A leaves it one
@@ -321,7 +325,29 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     // the first unrolled step wait for one more of the new tile loads.
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+v"(kf[kk]));
-    if (it + 1 < n_it) issue_loads(it + 1, buf ^ 1);  // that buffer was last read before the last barrier
+    // The direct loads of iteration it+1 (into the other stage, last read
+    // before the last barrier) go out one per k-step of the S / dP products
+    // below: issued at once, the workgroup's 72 loads queue at the address
+    // unit and stall each wave's issue for hundreds of cycles.  Resources
+    // and the lane offset are plain locals (see issue_tile).
+    const bool more = it + 1 < n_it;
+    const int ti1 = it_tile(it + 1);
+    const int h1 = it_head(it + 1), t1 = (qt0 + ti1) * kQB;
+    const bool live1 = more && ti1 < n_q;
+    const int64_t tile1 = ((static_cast<int64_t>(b) * s.q_len + t1) * s.h_q + h1) * D;
+    const int nb1 = live1 ? max(((s.q_len - t1) * row_stride - h1 * D) * 2, 0) : 0;
+    const __amdgpu_buffer_rsrc_t rs1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>((kgrp == 0 ? q : d_o) + tile1), 0, nb1, 0x00020000);
+    const int64_t st1 = (static_cast<int64_t>(b) * s.h_q + h1) * s.q_len + t1;
+    const __amdgpu_buffer_rsrc_t rst1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(rowstat + 2 * st1), 0, live1 ? max((s.q_len - t1) * 8, 0) : 0, 0x00020000);
+    char* hb1 = (buf == 1 ? stage0 : stage1) + hsub * L::head;
+    char* dst1 = hb1 + kgrp * (kQB * L::QP);
+    int ln1 = lane;
+    asm volatile("" : "+v"(ln1));
+    const int rbytes = row_stride * 2;
+    const int off01 = (ln1 / CH) * rbytes + (((ln1 % CH) ^ qswz<D>(ln1 / CH)) << 4);
+    static_assert(NCH <= KK, "at most one direct load per k-step");
 
     f32x16 sacc, pacc;
 #pragma unroll
@@ -335,6 +361,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + pos);
         const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sdO + pos);
         const bf16x8 bv = *reinterpret_cast<const bf16x8*>(sV + pos);
+        if (more && kk < NCH) {
+          const int voff = (off01 ^ (qswz<D>((kk * RPL) & 15) << 4)) + kk * RPL * rbytes;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs1, (lds_void*)(dst1 + kk * 64 * 16), 16, voff, 0, 0, 0);
+          if (kk == 0 && kgrp == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rst1, (lds_void*)(hb1 + 2 * kQB * L::QP), 4, lane * 4, 0, 0, 0);
+        }
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, bv, pacc, 0, 0, 0);
       }

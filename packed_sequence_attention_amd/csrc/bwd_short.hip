@@ -223,8 +223,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
   // Direct loads of the Q / dO block of iteration it into stage buf: chunk
   // ci = i * 256 + tid of each tensor lands at LDS chunk ci, so each lane
   // fetches the global chunk that belongs there under the swizzle.  Rows
-  // past the chunk read as zero.
-  auto issue_tile = [&](int it, int buf) __attribute__((always_inline)) {
+  // past the chunk read as zero.  Loads p0 .. p1-1 of the wave's 2 * PER_T
+  // (tensor-major), so that the loop can spread them over its products.
+  auto issue_tile = [&](int it, int buf, int p0, int p1) __attribute__((always_inline)) {
     char* dst = buf == 0 ? st0 : st1;
     const int ib = it / G, h = g * G + it % G;
     const int trow0 = t0 + ib * kSB;
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
           const_cast<uint16_t*>((tensor == 0 ? q : d_o) + tile0), 0, nbytes, 0x00020000);
 #pragma unroll
       for (int i = 0; i < L::PER_T; ++i) {
+        if (tensor * L::PER_T + i < p0 || tensor * L::PER_T + i >= p1) continue;
         const int cw = i * kThreads + wk * 64;  // the wave's first chunk of the tensor (uniform)
         const int lc = cw + lane;
         const int r = lc / L::CH, pc = (lc % L::CH) ^ swz<D>(r);
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
     lsev = lse[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t];
   };
 
-  issue_tile(0, 0);  // (n_it >= 1: a bin has a row)
+  issue_tile(0, 0, 0, 2 * L::PER_T);  // (n_it >= 1: a bin has a row)
   load_o(0);
   // K rows of this wave's key block into LDS (swizzled) and V fragments
   // (B operand of dP) in registers; keys past the bin are zero.
@@ -338,8 +340,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
     const char* sQ = buf == 0 ? st0 : st1;
     const char* sdO = sQ + L::qtile;
     // The next block goes to the other stage (last read before the last
-    // barrier).
-    if (it + 1 < n_it) issue_tile(it + 1, buf ^ 1);
+    // barrier), one load per k-step of the key phase's S / dP products
+    // (all at once on a wave whose key block no row of this block attends).
+    const bool more = it + 1 < n_it;
+    static_assert(2 * L::PER_T <= KK, "one direct load per k-step covers the block");
     store_pending();
     // Per-lane LDS offsets from an opaque copy of the lane index: hoisted
     // out of the loop, they would hold registers that the dK / dV
@@ -376,6 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
 
     // Key phase: S, dP, softmax and dS for this wave's key block; dV, dK.
     const bool live = wqlo < trow0 + kSB && wqhi > trow0;
+    if (!live && more) issue_tile(it + 1, buf ^ 1, 0, 2 * L::PER_T);
     if (live) {
       f32x16 sacc, pacc;
 #pragma unroll
@@ -387,6 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_short_kernel(
         const bf16x8 aq = *reinterpret_cast<const bf16x8*>(sQ + pos);
         const bf16x8 ao = *reinterpret_cast<const bf16x8*>(sdO + pos);
         const bf16x8 bk = *reinterpret_cast<const bf16x8*>(sK + kpos_l);
+        if (more && kk < 2 * L::PER_T) issue_tile(it + 1, buf ^ 1, kk, kk + 1);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, bk, sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, vf[kk], pacc, 0, 0, 0);
         // LDS reads at most two k-steps ahead of their products
