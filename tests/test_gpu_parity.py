@@ -197,6 +197,11 @@ SMALL = [
     ("bf16", [_rand_docs(20, 500, hi=300)], 500, 37, 400, 4, 4, 256),
     ("bf16", [_rand_docs(21, 600, hi=250)], 600, 0, 600, 4, 2, 256),
     ("bf16", [[1, 2, 3, 300, 1, 200]], 520, 0, 520, 2, 2, 64),
+    # GQA 16:1 (the dK/dV kernel's four rounds of four heads), three batch
+    # rows with a one-row chunk, and a 32:1 group at head_dim 64
+    ("bf16", [_rand_docs(22, 300, hi=200)], 300, 0, 300, 16, 1, 128),
+    ("bf16", [_rand_docs(23, 260), _rand_docs(24, 260, fill=200), _rand_docs(25, 260)], 260, 13, 1, 4, 2, 64),
+    ("bf16", [_rand_docs(26, 330, hi=150), _rand_docs(27, 330)], 330, 0, 330, 32, 1, 64),
 ]
 
 
