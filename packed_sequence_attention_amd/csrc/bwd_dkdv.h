@@ -276,6 +276,30 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     issue_tile(it_head(it), (qt0 + ti) * kQB, buf, ti < n_q);
   };
 
+  // No local row attends any of the workgroup's keys (keys of the K/V
+  // buffer outside every document of the chunk): their dK and dV are zero,
+  // written at once instead of summing four zero partials (the same bits).
+  // Wave (key group, hsub) writes the 32-column blocks db with db % 4 ==
+  // hsub of its keys' rows.  (n_q is the workgroup's, read from LDS after
+  // the barrier: every wave takes this branch or none.)
+  if (n_q == 0) {
+    if (key_ok) {
+      const uint2 z = make_uint2(0u, 0u);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        if (db % kHW != hsub) continue;
+        uint16_t* rk = dk + kv_row * D + kg * 4 + db * 32;
+        uint16_t* rv = dv + kv_row * D + kg * 4 + db * 32;
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          *reinterpret_cast<uint2*>(rk + jq * 8) = z;
+          *reinterpret_cast<uint2*>(rv + jq * 8) = z;
+        }
+      }
+    }
+    return;
+  }
+
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
