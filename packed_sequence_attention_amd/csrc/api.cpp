@@ -312,6 +312,8 @@ extern "C" bd_status blockdiag_attn_bwd(bd_dtype dtype, int32_t batch, int32_t s
                 dr, q, k, v, o, lse, d_o, meta->data, dq, dk, dv, static_cast<float*>(workspace), nullptr, nullptr};
   a.n_seg = meta->n_seg;
   a.max_seg_k = meta->max_seg_k;
+  a.live_lo = meta->kv_lo;
+  a.live_hi = meta->kv_hi;
   take_marks(&a.mark_start, &a.mark_stop);
   hipError_t e = mf ? bd::launch_bwd_mfma(a, s) : bd::launch_bwd_generic(a, s);
   if (e != hipSuccess) return fail(BD_ERR_HIP, "backward launch: %s", hipGetErrorString(e));

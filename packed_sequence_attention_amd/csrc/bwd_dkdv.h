@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int n_kt, int n_bg) {
+    uint16_t* __restrict__ dv, int n_kt, int n_bg, int live_lo, int live_hi) {
   constexpr int KK = D / 16;
   constexpr int DB = D / 32;
   constexpr int CH = D / 8;
@@ -128,6 +128,32 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
   // kv_len) of every row (key tiles are counted from kv_begin).
   const bool key_ok = key < s.kv_begin + s.kv_len;
   const int64_t kv_row = (static_cast<int64_t>(b) * s.kv_len + (key - s.kv_begin)) * s.h_kv + g;
+
+  // Zero dK and dV rows of this lane's key: wave (key group, hsub) writes
+  // the 32-column blocks db with db % 4 == hsub (the same bits as summing
+  // four zero partials).
+  auto write_zero_rows = [&]() {
+    if (!key_ok) return;
+    const uint2 z = make_uint2(0u, 0u);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      if (db % kHW != hsub) continue;
+      uint16_t* rk = dk + kv_row * D + kg * 4 + db * 32;
+      uint16_t* rv = dv + kv_row * D + kg * 4 + db * 32;
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        *reinterpret_cast<uint2*>(rk + jq * 8) = z;
+        *reinterpret_cast<uint2*>(rv + jq * 8) = z;
+      }
+    }
+  };
+  // Keys outside [live_lo, live_hi) (the positions any local row of any
+  // batch row attends, known on the host) are attended by no row: zero at
+  // once, before any load.  (Uniform over the workgroup: no barrier yet.)
+  if (key0 + kKB <= live_lo || key0 >= live_hi) {
+    write_zero_rows();
+    return;
+  }
 
   // Local rows attending this lane's key: [a0, a1) when a1 > a0 (loaded
   // here, used after the other prologue loads have been issued).
@@ -276,27 +302,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(
     issue_tile(it_head(it), (qt0 + ti) * kQB, buf, ti < n_q);
   };
 
-  // No local row attends any of the workgroup's keys (keys of the K/V
-  // buffer outside every document of the chunk): their dK and dV are zero,
-  // written at once instead of summing four zero partials (the same bits).
-  // Wave (key group, hsub) writes the 32-column blocks db with db % 4 ==
-  // hsub of its keys' rows.  (n_q is the workgroup's, read from LDS after
-  // the barrier: every wave takes this branch or none.)
+  // No local row attends any of the workgroup's keys: their dK and dV are
+  // zero, written at once instead of summing four zero partials.  (n_q is
+  // the workgroup's, read from LDS after the barrier: every wave takes this
+  // branch or none.)
   if (n_q == 0) {
-    if (key_ok) {
-      const uint2 z = make_uint2(0u, 0u);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if (db % kHW != hsub) continue;
-        uint16_t* rk = dk + kv_row * D + kg * 4 + db * 32;
-        uint16_t* rv = dv + kv_row * D + kg * 4 + db * 32;
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          *reinterpret_cast<uint2*>(rk + jq * 8) = z;
-          *reinterpret_cast<uint2*>(rv + jq * 8) = z;
-        }
-      }
-    }
+    write_zero_rows();
     return;
   }
 
@@ -626,7 +637,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t st) {
   bwd_dkdv_kernel<D, DROP><<<dim3(static_cast<unsigned>(grid)), 512, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.rowstat, m,
-      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg);
+      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg, a.live_lo, a.live_hi);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return mark(a.mark_stop, st);

@@ -56,6 +56,9 @@ struct BwdArgs {
   hipEvent_t mark_stop;
   int n_seg = 0;        // segments of the table the metadata was built from
   int max_seg_k = -1;   // most keys of one segment (-1: unknown)
+  // Key positions any local row of any batch row attends lie in [live_lo,
+  // live_hi) (the metadata descriptor's window); other keys' dK/dV are zero.
+  int live_lo = 0, live_hi = 0x7fffffff;
 };
 
 // Metadata expansion (segment table -> per-row / per-key bounds).  With
