@@ -41,8 +41,9 @@
 // chunk c ^ f(r), with f chosen so that 16 rows of a row read and 4 rows x 4
 // chunks of a transpose read all land on distinct banks.  Q / dO / LSE /
 // delta of the next query tile of each head are loaded straight into the
-// other half of an LDS double buffer (LDS-DMA) while the current one is
-// processed; one barrier per iteration.
+// other half of an LDS double buffer (LDS-DMA), one load per k-step of the
+// current tile's S / dP products; two barriers per iteration (the ping-pong
+// of the loop below).
 #pragma once
 
 #include <limits.h>
