@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void bwd_dkdv256_kernel(
     AttnShape s, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ rowstat, MetaView m, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int n_kt, int n_bg) {
+    uint16_t* __restrict__ dv, int n_kt, int n_bg, int live_lo, int live_hi) {
   constexpr int KK = kD / 16;
   constexpr int DB = kCH / 32;  // 32-column blocks of this workgroup's dK / dV
   __shared__ __attribute__((aligned(16))) char stage0[kStage];
@@ -94,6 +94,25 @@ __global__ __launch_bounds__(kWaves * 64, 1) void bwd_dkdv256_kernel(
   // kv_len) of every row (key tiles are counted from kv_begin).
   const bool key_ok = key < s.kv_begin + s.kv_len;
   const int64_t kv_row = (static_cast<int64_t>(b) * s.kv_len + (key - s.kv_begin)) * s.h_kv + g;
+  // Keys outside [live_lo, live_hi) (the positions any local row attends,
+  // known on the host) are attended by no row: their columns of dK and dV
+  // are zero, written before any load (the same bits as the products' sums
+  // of nothing; uniform over the workgroup, no barrier reached yet).
+  if (key0 + kKB <= live_lo || key0 >= live_hi) {
+    if (key_ok) {
+      const uint2 z = make_uint2(0u, 0u);
+      uint16_t* dkr = dk + kv_row * kD + ch * kCH + kg * 4;
+      uint16_t* dvr = dv + kv_row * kD + ch * kCH + kg * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          *reinterpret_cast<uint2*>(dkr + db * 32 + jq * 8) = z;
+          *reinterpret_cast<uint2*>(dvr + db * 32 + jq * 8) = z;
+        }
+    }
+    return;
+  }
 
   int a0 = 0, a1 = 0;  // local rows attending this lane's key: [a0, a1) when a1 > a0
   if (key_ok) {
@@ -375,7 +394,7 @@ hipError_t dkdv256_t(const BwdArgs& a, hipStream_t st) {
   bwd_dkdv256_kernel<DROP><<<dim3(static_cast<unsigned>(grid)), kWaves * 64, 0, st>>>(
       s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
       static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.d_o), a.rowstat, m,
-      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg);
+      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), n_kt, n_bg, a.live_lo, a.live_hi);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return mark(a.mark_stop, st);
