@@ -44,18 +44,33 @@ __device__ __forceinline__ void load8(const uint16_t* p, float out[8]) {
   }
 }
 
-// dot(x_lds[0:D], row[0:D]) with the row read from global memory.
+// dot(x_lds[0:D], row[0:D]) with the row read from global memory (D a
+// multiple of 8).  The loads of up to 64 elements go out together before
+// their products (one memory round trip per 64 elements instead of one per
+// 8); chunks at or past D re-read the row's last chunk and are skipped, so
+// the products are the same fmas in the same order d = 0, 1, ...
 template <typename T>
 __device__ __forceinline__ float dot_row(const float* x_lds, const T* row, int D) {
   float acc = 0.f;
-  for (int d = 0; d < D; d += 8) {
-    float r[8];
-    load8(row + d, r);
+  for (int d0 = 0; d0 < D; d0 += 64) {
+    float r[8][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(x_lds[d + e], r[e], acc);
+    for (int c = 0; c < 8; ++c) load8(row + min(d0 + 8 * c, D - 8), r[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (d0 + 8 * c >= D) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(x_lds[d0 + 8 * c + e], r[c][e], acc);
+    }
   }
   return acc;
 }
+
+// Rows of a sweep whose loads are issued together (the kernels' inner
+// loops over the keys or rows of a 64-block): one memory round trip per
+// sweep instead of one per row; the accumulation order is the rows' own
+// order.  (Wider sweeps measured no faster and took more registers.)
+constexpr int kSweep = 8;
 
 constexpr int kWaves = 4;
 constexpr int kMaxD = 256;
@@ -105,13 +120,26 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(AttnShape s, const T* 
     const int n = min(64, hi - j0);
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] *= alpha;
-    for (int jj = 0; jj < n; ++jj) {
-      const float pj = sp[wave][jj];
-      const T* vrow = v + ((kv_base + j0 + jj) * s.h_kv + g) * D;
+    for (int jb = 0; jb < n; jb += kSweep) {
+      // kSweep V rows loaded at once (rows past n re-read row n - 1 and are
+      // skipped), then accumulated in key order.
+      float vv[kSweep][NR];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int d = lane + 64 * r;
-        if (d < D) acc[r] = fmaf(pj, Elem<T>::load(vrow + d), acc[r]);
+      for (int u = 0; u < kSweep; ++u) {
+        const T* vrow = v + ((kv_base + j0 + min(jb + u, n - 1)) * s.h_kv + g) * D;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int d = lane + 64 * r;
+          vv[u][r] = d < D ? Elem<T>::load(vrow + d) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSweep; ++u) {
+        if (jb + u >= n) break;
+        const float pj = sp[wave][jb + u];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          if (lane + 64 * r < D) acc[r] = fmaf(pj, vv[u][r], acc[r]);
       }
     }
     mrun = mnew;
@@ -180,13 +208,24 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
     sp[wave][lane] = ds;
     wave_sync();
     const int n = min(64, hi - j0);
-    for (int jj = 0; jj < n; ++jj) {
-      const float dsj = sp[wave][jj];
-      const T* krow = k + ((kv_base + j0 + jj) * s.h_kv + g) * D;
+    for (int jb = 0; jb < n; jb += kSweep) {
+      float kv[kSweep][NR];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int d = lane + 64 * r;
-        if (d < D) acc[r] = fmaf(dsj, Elem<T>::load(krow + d), acc[r]);
+      for (int u = 0; u < kSweep; ++u) {
+        const T* krow = k + ((kv_base + j0 + min(jb + u, n - 1)) * s.h_kv + g) * D;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int d = lane + 64 * r;
+          kv[u][r] = d < D ? Elem<T>::load(krow + d) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kSweep; ++u) {
+        if (jb + u >= n) break;
+        const float dsj = sp[wave][jb + u];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          if (lane + 64 * r < D) acc[r] = fmaf(dsj, kv[u][r], acc[r]);
       }
     }
     wave_sync();
@@ -256,15 +295,28 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
       sds[wave][lane] = ds;
       wave_sync();
       const int n = min(64, qhi - t0);
-      for (int tt = 0; tt < n; ++tt) {
-        const float pt = sp[wave][tt], dst = sds[wave][tt];
-        const int64_t row = ((static_cast<int64_t>(b) * s.q_len + t0 + tt) * s.h_q + h) * D;
+      for (int tb = 0; tb < n; tb += kSweep) {
+        float xo[kSweep][NR], xq[kSweep][NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int d = lane + 64 * r;
-          if (d < D) {
-            adv[r] = fmaf(pt, Elem<T>::load(d_o + row + d), adv[r]);
-            adk[r] = fmaf(dst, Elem<T>::load(q + row + d), adk[r]);
+        for (int u = 0; u < kSweep; ++u) {
+          const int64_t row = ((static_cast<int64_t>(b) * s.q_len + t0 + min(tb + u, n - 1)) * s.h_q + h) * D;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            const int d = lane + 64 * r;
+            xo[u][r] = d < D ? Elem<T>::load(d_o + row + d) : 0.f;
+            xq[u][r] = d < D ? Elem<T>::load(q + row + d) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kSweep; ++u) {
+          if (tb + u >= n) break;
+          const float pt = sp[wave][tb + u], dst = sds[wave][tb + u];
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            if (lane + 64 * r < D) {
+              adv[r] = fmaf(pt, xo[u][r], adv[r]);
+              adk[r] = fmaf(dst, xq[u][r], adk[r]);
+            }
           }
         }
       }
