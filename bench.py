@@ -214,8 +214,8 @@ def main():
                          "reference for HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU's share only: run it with --gpus 1 (the multi-GPU exchange "
-              "around the kernel is not part of this build)", file=sys.stderr)
+        print("bench.py measures one GPU's share only: run it with --gpus 1 (the library holds the "
+              "single-GPU kernels; the multi-GPU K/V exchange around them is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

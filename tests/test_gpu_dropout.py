@@ -44,8 +44,8 @@ def _np(out):
 
 
 def _check_dropout(w, g, ref, t, p):
-    """The tolerances of the undropped path, except bf16 O: the benchmark spec
-    states no bound for dropout, so it is derived per element from the
+    """The tolerances of the undropped path, except bf16 O: the fixed bf16
+    bound is stated for the undropped output only, so here it is derived per element from the
     arithmetic -- the output's round-to-nearest (at most 2^-8 |O| for bf16)
     plus the bf16 rounding of the kept weights P * c that multiply V (at most
     2^-9 c max|v| summed over a row), plus 1e-3 for the float32 sums.  The
