@@ -259,6 +259,28 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
   const int nat_swz = rswz<D>(n);
   const int tr_row = 4 * kg + ((lane & 15) >> 2);
   const int tr_g = (lane >> 4) & 1, tr_s = lane & 3;
+  // Per-lane LDS offsets, one integer per read (the compiler keeps these live
+  // across the loop; at head_dim 256 one per read pushed the Q / dO fragments
+  // out of the vector registers).  The swizzle only permutes the low four
+  // bits of the chunk index and depends on the row index mod 16, so
+  //   K / V row reads: chunk 2 kk + kg of row sb*32 + n; for kk >= 8 (chunks
+  //   16..31, head_dim 256) the offset of kk - 8 plus 256 bytes;
+  //   K^T transpose reads: rows 16 kk2 + tr_row (+ 8) of block sb, column
+  //   block db; blocks 4..7 at the offsets of blocks 0..3 plus 256 bytes,
+  //   and the row block sb*32 + 16 kk2 adds a multiple of 16 rows.
+  constexpr int KKR = KK < 8 ? KK : 8;
+  constexpr int DBT = DB < 4 ? DB : 4;
+  int rro[KKR];
+#pragma unroll
+  for (int kk = 0; kk < KKR; ++kk) rro[kk] = n * RP + (((2 * kk + kg) ^ nat_swz) << 4);
+  int tro[DBT][2];
+#pragma unroll
+  for (int db = 0; db < DBT; ++db) {
+    const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
+    const int half = (tr_s & 1) * 8;
+    tro[db][0] = tr_row * RP + ((chunk ^ rswz<D>(tr_row)) << 4) + half;
+    tro[db][1] = (tr_row + 8) * RP + ((chunk ^ rswz<D>(tr_row + 8)) << 4) + half;
+  }
 
   if (kmax_g > kmin_g) {
     // kt1 >= (kmax - 1) / kBN: extra tiles are fully masked; none before the
@@ -279,24 +301,22 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
         f32x16 sacc, pacc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[j] = pacc[j] = 0.f;
-        const int rown = sb * 32 + n;
         // K / V row reads two k-steps ahead of their products (the
         // compiler, left alone, keeps one pair in flight and each pair of
         // products waits for its reads).
         constexpr int PF = D == 256 ? 1 : 2;
+        auto rpos = [&](int kk) { return rro[kk & 7] + (kk >> 3) * 256 + sb * 32 * RP; };
         bf16x8 ak[KK], av[KK];
 #pragma unroll
         for (int kk = 0; kk < PF; ++kk) {
-          const int pos = rown * RP + (((2 * kk + kg) ^ nat_swz) << 4);
-          ak[kk] = *reinterpret_cast<const bf16x8*>(sK + pos);
-          av[kk] = *reinterpret_cast<const bf16x8*>(sV + pos);
+          ak[kk] = *reinterpret_cast<const bf16x8*>(sK + rpos(kk));
+          av[kk] = *reinterpret_cast<const bf16x8*>(sV + rpos(kk));
         }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           if (kk + PF < KK) {
-            const int pos = rown * RP + (((2 * (kk + PF) + kg) ^ nat_swz) << 4);
-            ak[kk + PF] = *reinterpret_cast<const bf16x8*>(sK + pos);
-            av[kk + PF] = *reinterpret_cast<const bf16x8*>(sV + pos);
+            ak[kk + PF] = *reinterpret_cast<const bf16x8*>(sK + rpos(kk + PF));
+            av[kk + PF] = *reinterpret_cast<const bf16x8*>(sV + rpos(kk + PF));
           }
           if (sb == 0 && kk % LSTEP == 0) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk / LSTEP, pre);
           __builtin_amdgcn_sched_barrier(0);
@@ -327,11 +347,8 @@ __global__ __launch_bounds__(256, kDqOcc<D>) void bwd_dq_kernel(
         constexpr int NT = 2 * DB, PFT = D == 256 ? 1 : 2;
         auto kread = [&](int st_) {
           const int kk2 = st_ / DB, db = st_ % DB;
-          const int ra = sb * 32 + 16 * kk2 + tr_row, rb = ra + 8;
-          const int chunk = 4 * db + 2 * tr_g + (tr_s >> 1);
-          const int half = (tr_s & 1) * 8;
-          return lds_tr_pair(sK + ra * RP + ((chunk ^ rswz<D>(ra)) << 4) + half,
-                             sK + rb * RP + ((chunk ^ rswz<D>(rb)) << 4) + half);
+          const int r1 = (sb * 32 + 16 * kk2) * RP + (db >> 2) * 256;
+          return lds_tr_pair(sK + (tro[db & 3][0] + r1), sK + (tro[db & 3][1] + r1));
         };
         bf16x8 kq[NT];
 #pragma unroll
