@@ -30,8 +30,16 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 # form of the MFMA instructions (AGPRs then only hold spilled values).
 # The head_dim 64 instantiation of that kernel is also built with the
 # max-ILP scheduler (measured faster there, slower at head_dim 128).
+# The dQ kernel file takes the VGPR form too: at head_dim 256 (one wave per
+# SIMD, 512 registers) the default kept one of the Q / dO fragment arrays in
+# AGPRs and copied it back before every product (about four copies per
+# matrix instruction in the loop); with the VGPR form the loop holds 41
+# copies for 96 products and the kernel runs 17 % faster.  Its head_dim 64
+# and 128 code is the same either way.  (The head_dim 256 dK/dV kernel
+# measured slower with it.)
 EXTRA = {
     "bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "bwd_dkdv64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
