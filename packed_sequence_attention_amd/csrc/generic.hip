@@ -44,45 +44,70 @@ __device__ __forceinline__ void load8(const uint16_t* p, float out[8]) {
   }
 }
 
-// dot(x_lds[0:D], row[0:D]) with the row read from global memory (D a
-// multiple of 8).  The loads of up to 64 elements go out together before
-// their products (one memory round trip per 64 elements instead of one per
-// 8); chunks at or past D re-read the row's last chunk and are skipped, so
-// the products are the same fmas in the same order d = 0, 1, ...
+// Work layout.  A wave owns one query row (forward, dQ) or one key (dK/dV)
+// and sweeps its partners (the row's keys, the key's rows) in blocks of 64,
+// one partner per lane, anchored at the row's document start (the key's
+// first attending row), so a row's arithmetic does not depend on the chunk
+// or on the K/V window.  Each lane loads its partner's rows once per block
+// -- every load of the block goes out together, one memory round trip --
+// and uses them twice: for its dot products (score, dP) and for the
+// weighted sums over the block's partners (P V, dS K, P dO, dS Q), which
+// are lane transposes: lane_sum64 adds the 64 lanes' vectors so that lane l
+// ends with column l.
+
+// Columns [c0, c0 + 64) of a row of D elements (D a multiple of 8); groups
+// at or past D re-read the row's last group (their values are not used).
 template <typename T>
-__device__ __forceinline__ float dot_row(const float* x_lds, const T* row, int D) {
-  float acc = 0.f;
-  for (int d0 = 0; d0 < D; d0 += 64) {
-    float r[8][8];
+__device__ __forceinline__ void load_cols64(const T* row, int c0, int D, float x[64]) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) load8(row + min(d0 + 8 * c, D - 8), r[c]);
+  for (int g = 0; g < 8; ++g) load8(row + min(c0 + 8 * g, D - 8), x + 8 * g);
+}
+
+// acc + sum over d in [c0, min(c0 + 64, D)) of x_lds[d] * x[d - c0], in
+// column order.
+__device__ __forceinline__ float dot_cols64(const float* x_lds, const float x[64], int c0, int D, float acc) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (d0 + 8 * c >= D) break;
+  for (int g = 0; g < 8; ++g) {
+    if (c0 + 8 * g >= D) break;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf(x_lds[d0 + 8 * c + e], r[c][e], acc);
-    }
+    for (int e = 0; e < 8; ++e) acc = fmaf(x_lds[c0 + 8 * g + e], x[8 * g + e], acc);
   }
   return acc;
 }
 
-// Rows of a sweep whose loads are issued together (the kernels' inner
-// loops over the keys or rows of a 64-block): one memory round trip per
-// sweep instead of one per row; the accumulation order is the rows' own
-// order.  (Wider sweeps measured no faster and took more registers.)
-constexpr int kSweep = 8;
+// Sum over the wave's 64 lanes of the vectors x[0..64) (one per lane): lane
+// l returns the total of element l.  Recursive halving: at offset O each
+// lane holds 2 O partial sums, keeps the half its lane bit O selects, and
+// adds the partner lane's (l ^ O) copy of that half; after the six steps
+// lane l holds element l.  x is used as scratch.  (The steps are templates
+// so that every index is a constant and x stays in registers.)
+template <int O>
+__device__ __forceinline__ void lane_sum_step(float x[64], int lane) {
+  const bool up = (lane & O) != 0;
+#pragma unroll
+  for (int i = 0; i < O; ++i) {
+    const float send = up ? x[i] : x[O + i];
+    const float keep = up ? x[O + i] : x[i];
+    x[i] = keep + __shfl_xor(send, O, 64);
+  }
+  if constexpr (O > 1) lane_sum_step<O / 2>(x, lane);
+}
+__device__ __forceinline__ float lane_sum64(float x[64], int lane) {
+  lane_sum_step<32>(x, lane);
+  return x[0];
+}
 
 constexpr int kWaves = 4;
 constexpr int kMaxD = 256;
 
-// One wave per (b, query head, local row).
+// One wave per (b, query head, local row); lane l accumulates output columns
+// l + 64 r.
 template <typename T, int NR>
 __global__ __launch_bounds__(256) void fwd_generic_kernel(AttnShape s, const T* __restrict__ q,
                                                           const T* __restrict__ k,
                                                           const T* __restrict__ v, MetaView m,
                                                           T* __restrict__ o, float* __restrict__ lse) {
   __shared__ float sq[kWaves][kMaxD];
-  __shared__ float sp[kWaves][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   const int64_t total = static_cast<int64_t>(s.batch) * s.q_len * s.h_q;
@@ -105,45 +130,38 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(AttnShape s, const T* 
   for (int r = 0; r < NR; ++r) acc[r] = 0.f;
   for (int j0 = lo; j0 < hi; j0 += 64) {
     const int j = j0 + lane;
-    float sc = -INFINITY;
-    if (j < hi) sc = s.scale * dot_row(sq[wave], k + ((kv_base + j) * s.h_kv + g) * D, D);
+    const bool in = j < hi;
+    const int64_t jr = ((kv_base + min(j, hi - 1)) * s.h_kv + g) * D;  // lanes past hi re-read the last key
+    // Score, with V columns 0-63 loaded beside K (one round trip at
+    // head_dim <= 64; wider rows load V by 64 columns after the softmax).
+    float vx[64];
+    float sc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+      float kx[64];
+      load_cols64(k + jr, 64 * c, D, kx);
+      if (c == 0) load_cols64(v + jr, 0, D, vx);
+      sc = dot_cols64(sq[wave], kx, 64 * c, D, sc);
+    }
+    sc = in ? s.scale * sc : -INFINITY;
     const float mnew = fmaxf(mrun, wave_max(sc));  // finite: lane 0 is in range
-    const float p = (j < hi) ? expf(sc - mnew) : 0.f;
+    const float p = in ? expf(sc - mnew) : 0.f;
     const float alpha = expf(mrun - mnew);
     lrun = lrun * alpha + wave_sum(p);
     // dropout acts on the weights that multiply V, not on the row sum
-    sp[wave][lane] = (s.drop.thr != 0 && j < hi)
+    const float pw = (s.drop.thr != 0 && in)
                          ? p * keep_one(s.drop, static_cast<uint32_t>(s.row_offset + t), static_cast<uint32_t>(j),
                                         static_cast<uint32_t>(b * s.h_q + h))
                          : p;
-    wave_sync();
-    const int n = min(64, hi - j0);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] *= alpha;
-    for (int jb = 0; jb < n; jb += kSweep) {
-      // kSweep V rows loaded at once (rows past n re-read row n - 1 and are
-      // skipped), then accumulated in key order.
-      float vv[kSweep][NR];
+    for (int c = 0; c < NR; ++c) {
+      if (c > 0) load_cols64(v + jr, 64 * c, D, vx);
+      float x[64];
 #pragma unroll
-      for (int u = 0; u < kSweep; ++u) {
-        const T* vrow = v + ((kv_base + j0 + min(jb + u, n - 1)) * s.h_kv + g) * D;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int d = lane + 64 * r;
-          vv[u][r] = d < D ? Elem<T>::load(vrow + d) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kSweep; ++u) {
-        if (jb + u >= n) break;
-        const float pj = sp[wave][jb + u];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-          if (lane + 64 * r < D) acc[r] = fmaf(pj, vv[u][r], acc[r]);
-      }
+      for (int i = 0; i < 64; ++i) x[i] = pw * vx[i];
+      acc[c] = acc[c] * alpha + lane_sum64(x, lane);
     }
     mrun = mnew;
-    wave_sync();
   }
   const bool any = hi > lo;
   const float inv = any ? 1.f / lrun : 0.f;
@@ -157,7 +175,8 @@ __global__ __launch_bounds__(256) void fwd_generic_kernel(AttnShape s, const T* 
     lse[(static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t] = any ? mrun + logf(lrun) : -INFINITY;
 }
 
-// One wave per (b, query head, local row): dQ_i = scale * sum_j dS_ij k_j.
+// One wave per (b, query head, local row): dQ_i = scale * sum_j dS_ij k_j;
+// lane l accumulates columns l + 64 r.
 template <typename T, int NR>
 __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* __restrict__ q,
                                                          const T* __restrict__ k,
@@ -168,7 +187,6 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
                                                          T* __restrict__ dq) {
   __shared__ float sq[kWaves][kMaxD];
   __shared__ float sdo[kWaves][kMaxD];
-  __shared__ float sp[kWaves][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   const int64_t total = static_cast<int64_t>(s.batch) * s.q_len * s.h_q;
@@ -195,40 +213,36 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
   for (int r = 0; r < NR; ++r) acc[r] = 0.f;
   for (int j0 = lo; j0 < hi; j0 += 64) {
     const int j = j0 + lane;
+    const bool in = j < hi;
+    const int64_t kr = ((kv_base + min(j, hi - 1)) * s.h_kv + g) * D;
+    // K and V of the lane's key: the score and dP dots; K columns 0-63 stay
+    // for the dS K sum (wider rows reload K by 64 columns).
+    float kx[64];
+    float sdot = 0.f, dp = 0.f;
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+      float vx[64];
+      load_cols64(k + kr, 64 * c, D, kx);
+      load_cols64(v + kr, 64 * c, D, vx);
+      sdot = dot_cols64(sq[wave], kx, 64 * c, D, sdot);
+      dp = dot_cols64(sdo[wave], vx, 64 * c, D, dp);
+    }
     float ds = 0.f;
-    if (j < hi) {
-      const int64_t kr = ((kv_base + j) * s.h_kv + g) * D;
-      const float p = expf(s.scale * dot_row(sq[wave], k + kr, D) - lse_t);
-      float dp = dot_row(sdo[wave], v + kr, D);
+    if (in) {
+      const float p = expf(s.scale * sdot - lse_t);
       if (s.drop.thr != 0)  // the gradient reaching P is (dO . v_j) * Z * c
         dp *= keep_one(s.drop, static_cast<uint32_t>(s.row_offset + t), static_cast<uint32_t>(j),
                        static_cast<uint32_t>(b * s.h_q + h));
       ds = p * (dp - delta_t);
     }
-    sp[wave][lane] = ds;
-    wave_sync();
-    const int n = min(64, hi - j0);
-    for (int jb = 0; jb < n; jb += kSweep) {
-      float kv[kSweep][NR];
 #pragma unroll
-      for (int u = 0; u < kSweep; ++u) {
-        const T* krow = k + ((kv_base + j0 + min(jb + u, n - 1)) * s.h_kv + g) * D;
+    for (int c = 0; c < NR; ++c) {
+      if (NR > 1) load_cols64(k + kr, 64 * c, D, kx);
+      float x[64];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const int d = lane + 64 * r;
-          kv[u][r] = d < D ? Elem<T>::load(krow + d) : 0.f;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kSweep; ++u) {
-        if (jb + u >= n) break;
-        const float dsj = sp[wave][jb + u];
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-          if (lane + 64 * r < D) acc[r] = fmaf(dsj, kv[u][r], acc[r]);
-      }
+      for (int i = 0; i < 64; ++i) x[i] = ds * kx[i];
+      acc[c] += lane_sum64(x, lane);
     }
-    wave_sync();
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
@@ -239,7 +253,8 @@ __global__ __launch_bounds__(256) void dq_generic_kernel(AttnShape s, const T* _
 
 // One wave per (b, K/V head, key position): dV_j = sum_i P_ij dO_i and
 // dK_j = scale * sum_i dS_ij q_i over the group's query heads and the local
-// rows attending j.  Keys no row attends get zeros.
+// rows attending j; lane l accumulates columns l + 64 r.  Keys no row
+// attends get zeros.
 template <typename T, int NR>
 __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* __restrict__ q,
                                                           const T* __restrict__ k,
@@ -250,8 +265,6 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
                                                           T* __restrict__ dk, T* __restrict__ dv) {
   __shared__ float sk[kWaves][kMaxD];
   __shared__ float sv[kWaves][kMaxD];
-  __shared__ float sp[kWaves][64];
-  __shared__ float sds[kWaves][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   const int64_t total = static_cast<int64_t>(s.batch) * s.kv_len * s.h_kv;  // the window's keys
@@ -268,6 +281,7 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
   }
   wave_sync();
   const int qlo = m.key_qlo[bj], qhi = m.key_qhi[bj];
+  const uint32_t jpos = static_cast<uint32_t>(bj - static_cast<int64_t>(b) * s.seq_len);
   float adk[NR], adv[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) adk[r] = adv[r] = 0.f;
@@ -275,52 +289,48 @@ __global__ __launch_bounds__(256) void dkv_generic_kernel(AttnShape s, const T* 
     const int h = g * s.group + hh;
     for (int t0 = qlo; t0 < qhi; t0 += 64) {
       const int t = t0 + lane;
+      const bool in = t < qhi;
+      const int tc = min(t, qhi - 1);  // lanes past qhi re-read the last row
+      const int64_t row = ((static_cast<int64_t>(b) * s.q_len + tc) * s.h_q + h) * D;
+      const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + tc;
+      const float lse_r = lse[st], delta_r = rowstat[2 * st + 1];
+      // Q and dO of the lane's row: the score and dP dots; columns 0-63
+      // stay for the dS Q and P dO sums (wider rows reload them).
+      float qx[64], ox[64];
+      float sdot = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < NR; ++c) {
+        load_cols64(q + row, 64 * c, D, qx);
+        load_cols64(d_o + row, 64 * c, D, ox);
+        sdot = dot_cols64(sk[wave], qx, 64 * c, D, sdot);
+        dp = dot_cols64(sv[wave], ox, 64 * c, D, dp);
+      }
       float p = 0.f, ds = 0.f;
-      if (t < qhi) {
-        const int64_t row = ((static_cast<int64_t>(b) * s.q_len + t) * s.h_q + h) * D;
-        const int64_t st = (static_cast<int64_t>(b) * s.h_q + h) * s.q_len + t;
-        p = expf(s.scale * dot_row(sk[wave], q + row, D) - lse[st]);
-        float dp = dot_row(sv[wave], d_o + row, D);
+      if (in) {
+        p = expf(s.scale * sdot - lse_r);
         if (s.drop.thr != 0) {  // P * Z * c multiplies dO; the gradient reaching P is dP * Z * c
-          const float z = keep_one(s.drop, static_cast<uint32_t>(s.row_offset + t),
-                                   static_cast<uint32_t>(bj - static_cast<int64_t>(b) * s.seq_len),
+          const float z = keep_one(s.drop, static_cast<uint32_t>(s.row_offset + t), jpos,
                                    static_cast<uint32_t>(b * s.h_q + h));
-          ds = p * (dp * z - rowstat[2 * st + 1]);
+          ds = p * (dp * z - delta_r);
           p *= z;
         } else {
-          ds = p * (dp - rowstat[2 * st + 1]);
+          ds = p * (dp - delta_r);
         }
       }
-      sp[wave][lane] = p;
-      sds[wave][lane] = ds;
-      wave_sync();
-      const int n = min(64, qhi - t0);
-      for (int tb = 0; tb < n; tb += kSweep) {
-        float xo[kSweep][NR], xq[kSweep][NR];
 #pragma unroll
-        for (int u = 0; u < kSweep; ++u) {
-          const int64_t row = ((static_cast<int64_t>(b) * s.q_len + t0 + min(tb + u, n - 1)) * s.h_q + h) * D;
-#pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const int d = lane + 64 * r;
-            xo[u][r] = d < D ? Elem<T>::load(d_o + row + d) : 0.f;
-            xq[u][r] = d < D ? Elem<T>::load(q + row + d) : 0.f;
-          }
+      for (int c = 0; c < NR; ++c) {
+        if (NR > 1) {
+          load_cols64(q + row, 64 * c, D, qx);
+          load_cols64(d_o + row, 64 * c, D, ox);
         }
+        float x[64];
 #pragma unroll
-        for (int u = 0; u < kSweep; ++u) {
-          if (tb + u >= n) break;
-          const float pt = sp[wave][tb + u], dst = sds[wave][tb + u];
+        for (int i = 0; i < 64; ++i) x[i] = p * ox[i];
+        adv[c] += lane_sum64(x, lane);
 #pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            if (lane + 64 * r < D) {
-              adv[r] = fmaf(pt, xo[u][r], adv[r]);
-              adk[r] = fmaf(dst, xq[u][r], adk[r]);
-            }
-          }
-        }
+        for (int i = 0; i < 64; ++i) x[i] = ds * qx[i];
+        adk[c] += lane_sum64(x, lane);
       }
-      wave_sync();
     }
   }
 #pragma unroll
