@@ -47,14 +47,42 @@ template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16_bits(x); }
 };
 
+// Partner exchanges on the vector ALU (all 64 lanes active), without the
+// LDS round trip of a bpermute: lane_swap<O> returns (own value, partner's
+// value) in either order, the partner being l ^ 32 and l ^ 16 (the permlane
+// swaps), l ^ 15 (row mirror), l ^ 7 (half-row mirror), l ^ 2 and l ^ 1
+// (quad permutes).  Those six masks span all six lane bits, so combining
+// over them in turn reaches every lane once: a wave-wide reduction whose
+// result is the same bits in every lane (each pair computes a + b and b + a).
+template <int O>
+__device__ __forceinline__ float2 lane_swap(float x) {
+  if constexpr (O >= 16) {
+    const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    constexpr int ctrl = O == 8 ? 0x140 : O == 4 ? 0x141 : O == 2 ? 0x4E : 0xB1;
+    return make_float2(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false)));
+  }
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  float2 r;
+  r = lane_swap<32>(x); x = fmaxf(r.x, r.y);
+  r = lane_swap<16>(x); x = fmaxf(r.x, r.y);
+  r = lane_swap<8>(x); x = fmaxf(r.x, r.y);
+  r = lane_swap<4>(x); x = fmaxf(r.x, r.y);
+  r = lane_swap<2>(x); x = fmaxf(r.x, r.y);
+  r = lane_swap<1>(x); x = fmaxf(r.x, r.y);
   return x;
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  float2 r;
+  r = lane_swap<32>(x); x = r.x + r.y;
+  r = lane_swap<16>(x); x = r.x + r.y;
+  r = lane_swap<8>(x); x = r.x + r.y;
+  r = lane_swap<4>(x); x = r.x + r.y;
+  r = lane_swap<2>(x); x = r.x + r.y;
+  r = lane_swap<1>(x); x = r.x + r.y;
   return x;
 }
 // Lane l and lane l ^ 32 combined (all 64 lanes active): v_permlane32_swap

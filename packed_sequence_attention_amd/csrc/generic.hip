@@ -78,17 +78,37 @@ __device__ __forceinline__ float dot_cols64(const float* x_lds, const float x[64
 // Sum over the wave's 64 lanes of the vectors x[0..64) (one per lane): lane
 // l returns the total of element l.  Recursive halving: at offset O each
 // lane holds 2 O partial sums, keeps the half its lane bit O selects, and
-// adds the partner lane's (l ^ O) copy of that half; after the six steps
-// lane l holds element l.  x is used as scratch.  (The steps are templates
-// so that every index is a constant and x stays in registers.)
+// adds its partner's copy of that half (the partner differs from l in bit O
+// and agrees above it: l ^ 32, l ^ 16, l ^ 15, l ^ 7, l ^ 2, l ^ 1); after
+// the six steps lane l holds element l.  x is used as scratch.  (The steps are templates
+// so that every index is a constant and x stays in registers.)  The
+// exchanges are vector-ALU lane permutes, without the LDS round trip of a
+// bpermute.
 template <int O>
 __device__ __forceinline__ void lane_sum_step(float x[64], int lane) {
-  const bool up = (lane & O) != 0;
+  if constexpr (O >= 16) {
+    // v_permlane32_swap / v_permlane16_swap of (x[i], x[O + i]) hands every
+    // lane its own kept value and its partner's copy of it.
 #pragma unroll
-  for (int i = 0; i < O; ++i) {
-    const float send = up ? x[i] : x[O + i];
-    const float keep = up ? x[O + i] : x[i];
-    x[i] = keep + __shfl_xor(send, O, 64);
+    for (int i = 0; i < O; ++i) {
+      const uint32_t a = __float_as_uint(x[i]), b = __float_as_uint(x[O + i]);
+      const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(a, b, false, false)
+                             : __builtin_amdgcn_permlane16_swap(a, b, false, false);
+      x[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  } else {
+    // partners by DPP: row mirror (l ^ 15) for bit 3, half-row mirror
+    // (l ^ 7) for bit 2, quad permutes for bits 1 and 0; each partner
+    // differs in the selecting bit and shares the higher ones.
+    constexpr int ctrl = O == 8 ? 0x140 : O == 4 ? 0x141 : O == 2 ? 0x4E : 0xB1;
+    const bool up = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < O; ++i) {
+      const float send = up ? x[i] : x[O + i];
+      const float keep = up ? x[O + i] : x[i];
+      const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), ctrl, 0xF, 0xF, false));
+      x[i] = keep + recv;
+    }
   }
   if constexpr (O > 1) lane_sum_step<O / 2>(x, lane);
 }
