@@ -55,15 +55,20 @@ template <> struct Elem<uint16_t> {
 // over them in turn reaches every lane once: a wave-wide reduction whose
 // result is the same bits in every lane (each pair computes a + b and b + a).
 template <int O>
-__device__ __forceinline__ float2 lane_swap(float x) {
+__device__ __forceinline__ uint2 lane_swap_u(uint32_t x) {
   if constexpr (O >= 16) {
-    const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
-                           : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const auto r = O == 32 ? __builtin_amdgcn_permlane32_swap(x, x, false, false)
+                           : __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return make_uint2(r[0], r[1]);
   } else {
     constexpr int ctrl = O == 8 ? 0x140 : O == 4 ? 0x141 : O == 2 ? 0x4E : 0xB1;
-    return make_float2(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false)));
+    return make_uint2(x, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), ctrl, 0xF, 0xF, false)));
   }
+}
+template <int O>
+__device__ __forceinline__ float2 lane_swap(float x) {
+  const uint2 r = lane_swap_u<O>(__float_as_uint(x));
+  return make_float2(__uint_as_float(r.x), __uint_as_float(r.y));
 }
 __device__ __forceinline__ float wave_max(float x) {
   float2 r;
@@ -101,16 +106,17 @@ __device__ __forceinline__ float pair32_sum(float x) {
 // Wave-wide min / max (all 64 lanes active).  Every lane holds the result
 // after the butterfly; reading it from the first lane marks it uniform, so
 // it can feed scalar registers (buffer resources, loop bounds).
-__device__ __forceinline__ int wave_min_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
-  return __builtin_amdgcn_readfirstlane(x);
+// (The exchanges are those of wave_max above.)
+template <bool MIN, int O = 32>
+__device__ __forceinline__ int wave_minmax_i(int x) {
+  const uint2 r = lane_swap_u<O>(static_cast<uint32_t>(x));
+  const int a = static_cast<int>(r.x), b = static_cast<int>(r.y);
+  x = MIN ? min(a, b) : max(a, b);
+  if constexpr (O > 1) return wave_minmax_i<MIN, O / 2>(x);
+  else return x;
 }
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  return __builtin_amdgcn_readfirstlane(x);
-}
+__device__ __forceinline__ int wave_min_i(int x) { return __builtin_amdgcn_readfirstlane(wave_minmax_i<true>(x)); }
+__device__ __forceinline__ int wave_max_i(int x) { return __builtin_amdgcn_readfirstlane(wave_minmax_i<false>(x)); }
 
 // Attention dropout.  Keep decisions come from Philox4x32-10, the
 // counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel Random
