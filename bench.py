@@ -119,8 +119,13 @@ class HipEvents:
 
 
 def kernel_source_digest(name):
-    path = os.path.join(ROOT, "packed_sequence_attention_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 prefix of a kernel's source file followed by the shared device
+    header every kernel includes (its reductions and helpers are part of the
+    kernel's code)."""
+    h = hashlib.sha256()
+    for f in (name, "device_common.h"):
+        h.update(open(os.path.join(ROOT, "packed_sequence_attention_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(kernel, kernel_file, workload_tag):
