@@ -281,11 +281,33 @@ __global__ __launch_bounds__(256, kFwdOcc<D>) void fwd_mfma_kernel(AttnShape s, 
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
         const int rown = sb * 32 + n;
+        auto kread = [&](int kk) {
+          return *reinterpret_cast<const bf16x8*>(sK + rown * RP + (((2 * kk + kg) ^ nat_swz) << 4));
+        };
+        if constexpr (D <= 128) {
+          // K row reads two k-steps ahead of their products (left alone, the
+          // compiler issues each read after the previous product and every
+          // product waits for its read).  Not at head_dim 256, whose
+          // registers are not free for it.
+          constexpr int KPF = 2;
+          bf16x8 ak[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sK + rown * RP + (((2 * kk + kg) ^ nat_swz) << 4));
-          if (sb == 0 && kk < 2 * L::NCH) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk, pre);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
+          for (int kk = 0; kk < KPF; ++kk) ak[kk] = kread(kk);
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + KPF < KK) ak[kk + KPF] = kread(kk + KPF);
+            if (sb == 0 && kk < 2 * L::NCH) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk, pre);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], qf[kk], sacc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 a = kread(kk);
+            if (sb == 0 && kk < 2 * L::NCH) issue_chunk(pre ? kt - 1 : kt, buf ^ 1, kk, pre);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
+          }
         }
         // sacc[j] = S[key k0 + sb*32 + (j/4)*8 + kg*4 + j%4][row n]
         if (!full) {
