@@ -202,6 +202,11 @@ SMALL = [
     ("bf16", [_rand_docs(22, 300, hi=200)], 300, 0, 300, 16, 1, 128),
     ("bf16", [_rand_docs(23, 260), _rand_docs(24, 260, fill=200), _rand_docs(25, 260)], 260, 13, 1, 4, 2, 64),
     ("bf16", [_rand_docs(26, 330, hi=150), _rand_docs(27, 330)], 330, 0, 330, 32, 1, 64),
+    # generic kernels at head_dims past 128 that are not multiples of 64: a
+    # partial third block of 64 columns and a fourth wholly past the row
+    # (float32, and bf16 at a head_dim the matrix-core kernels do not take)
+    ("f32", [_rand_docs(28, 220)], 220, 0, 220, 2, 1, 136),
+    ("bf16", [_rand_docs(29, 180, fill=170)], 180, 20, 160, 4, 4, 200),
 ]
 
 
