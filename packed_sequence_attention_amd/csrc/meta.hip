@@ -366,10 +366,10 @@ __device__ __forceinline__ void meta_one(const int32_t* table, int n_seg, int se
 // (m.q_order non-null) workgroup 0 builds it; the next one builds the bins;
 // the others write the bounds.
 
-// Tables of up to this many segments are staged in LDS by the workgroups
-// that build the query-tile order and the bins (their binary searches and
-// walks would otherwise wait on global memory at every step); larger ones
-// get no sorted order.
+// Tables of up to this many segments are staged in LDS by every workgroup
+// (the bounds' binary searches and the order and bin walks would otherwise
+// wait on global memory at every step); larger ones are searched in global
+// memory and get no sorted order and no bins.
 constexpr int kOrderStageSeg = kBinMaxSeg;
 
 __global__ void meta_kernel(const int32_t* __restrict__ table, int n_seg, int batch, int seq_len, int row_offset,
@@ -381,12 +381,12 @@ __global__ void meta_kernel(const int32_t* __restrict__ table, int n_seg, int ba
   __shared__ int32_t stage[3 * kOrderStageSeg + 2];
   const int ord = m.q_order != nullptr ? 1 : 0;
   const int wg = static_cast<int>(blockIdx.x);
+  const bool staged = n_seg <= kOrderStageSeg;
+  if (staged) {
+    for (int i = threadIdx.x; i < 3 * n_seg + 2; i += blockDim.x) stage[i] = table[i];
+    __syncthreads();
+  }
   if (wg < ord + 1) {
-    const bool staged = n_seg <= kOrderStageSeg;
-    if (staged) {
-      for (int i = threadIdx.x; i < 3 * n_seg + 2; i += blockDim.x) stage[i] = table[i];
-      __syncthreads();
-    }
     if (wg == ord) {
       // (an empty chunk has no bin section; a table too long to stage gets no bins)
       if (n_rows > 0) {
@@ -406,7 +406,8 @@ __global__ void meta_kernel(const int32_t* __restrict__ table, int n_seg, int ba
     }
     return;
   }
-  meta_one(table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m, static_cast<int64_t>(wg) - ord - 1);
+  meta_one(staged ? stage : table, n_seg, seq_len, row_offset, q_len, n_rows, n_keys, m,
+           static_cast<int64_t>(wg) - ord - 1);
 }
 
 // The table passed by value in the kernel arguments (small tables): no
